@@ -1,0 +1,233 @@
+/*
+ * CPU oracle for batched paged-attention decode.  TEST INFRASTRUCTURE ONLY:
+ * the parity tests, the smoke check and the benchmark's CPU-baseline leg are
+ * its only callers.  It shares no code, header or constant with the HIP
+ * library; both sides see only the same seeded inputs.
+ *
+ * What it follows (PhotonInfer README, zh-CN / fr / ja translations):
+ *   - "GPU-optimised kernels": batched paged attention over a block-level KV
+ *     cache, and a numerically stable softmax;
+ *   - "Technical details -> Paged attention": a block-level KV cache, per
+ *     sequence cache offsets (read as block tables), and one batched K/V
+ *     write for many sequences (read as a per-token slot mapping).
+ * The pages print no formula; the attention computed here is the textbook
+ * single-query decode step, out = softmax(scale * q K^T) V, with grouped-query
+ * heads: q head h reads KV head floor(h / (Hq/Hkv)).
+ *
+ * Layout (shared by K and V pools): [num_blocks, num_kv_heads, block_size,
+ * head_dim], contiguous.  slot = physical_block * block_size + offset.
+ *
+ * Arithmetic: every element is widened exactly to double, scores, maximum,
+ * exponentials, sums and the weighted sum of V are all formed in double, with
+ * one plain pass per output and no blocking or rescaling.  Sums run in token
+ * order, dot products in element order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum {
+    ORACLE_OK = 0,
+    ORACLE_ERR_ARG = 1,         /* bad sizes, dtype or null pointers        */
+    ORACLE_ERR_SLOT_RANGE = 2,  /* slot < -1 or slot >= num_blocks*bs        */
+    ORACLE_ERR_SLOT_DUP = 3,    /* two tokens write the same slot            */
+    ORACLE_ERR_BLOCK_RANGE = 4, /* a block id the sequence uses is out of range */
+    ORACLE_ERR_CTX = 5,         /* context length < 0 or > max_blocks*bs     */
+    ORACLE_ERR_HEADS = 6        /* num_q_heads not a multiple of num_kv_heads */
+};
+
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1 };
+
+/* IEEE 754 binary16 -> double, from the format's definition: 1 sign bit,
+ * 5 exponent bits (bias 15), 10 fraction bits; exponent 0 encodes zero and
+ * subnormals (fraction * 2^-24), exponent 31 encodes inf / NaN. */
+double oracle_half_to_double(uint16_t bits)
+{
+    const int sign = bits >> 15;
+    const int expo = (bits >> 10) & 0x1f;
+    const int frac = bits & 0x3ff;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24);
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(frac | 0x400), expo - 25);
+    return sign ? -mag : mag;
+}
+
+static double widen(const void *base, int64_t idx, int dtype)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    return oracle_half_to_double(((const uint16_t *)base)[idx]);
+}
+
+/* Cache write: for each token i with slot >= 0, copy the raw bytes of
+ * k[i, h, :] and v[i, h, :] into row (slot / bs, h, slot % bs) of the pools,
+ * for every KV head h.  Bytes are copied, never converted. */
+int oracle_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
+                          int64_t num_tokens, void *k_cache, void *v_cache,
+                          int64_t num_blocks, int64_t num_kv_heads, int64_t block_size,
+                          int64_t head_dim, int64_t elem_bytes)
+{
+    if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 ||
+        head_dim <= 0 || (elem_bytes != 2 && elem_bytes != 4))
+        return ORACLE_ERR_ARG;
+    if (num_tokens == 0)
+        return ORACLE_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+        return ORACLE_ERR_ARG;
+
+    const int64_t nslots = num_blocks * block_size;
+    unsigned char *seen = (unsigned char *)calloc((size_t)nslots, 1);
+    if (!seen)
+        return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        const int64_t s = slot_mapping[i];
+        if (s < -1 || s >= nslots) {
+            free(seen);
+            return ORACLE_ERR_SLOT_RANGE;
+        }
+        if (s >= 0) {
+            if (seen[s]) {
+                free(seen);
+                return ORACLE_ERR_SLOT_DUP;
+            }
+            seen[s] = 1;
+        }
+    }
+    free(seen);
+
+    const int64_t row_bytes = head_dim * elem_bytes;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        const int64_t s = slot_mapping[i];
+        if (s < 0)
+            continue;
+        const int64_t blk = s / block_size;
+        const int64_t off = s % block_size;
+        for (int64_t h = 0; h < num_kv_heads; ++h) {
+            const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_bytes;
+            const int64_t src = (i * num_kv_heads + h) * row_bytes;
+            memcpy((char *)k_cache + dst, (const char *)k + src, (size_t)row_bytes);
+            memcpy((char *)v_cache + dst, (const char *)v + src, (size_t)row_bytes);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Paged decode attention.
+ *   q            [B, Hq, D]           dtype
+ *   k/v_cache    [NB, Hkv, bs, D]     dtype
+ *   block_tables [B, max_blocks]      int32 (entries past ceil(ctx/bs) ignored)
+ *   context_lens [B]                  int32
+ *   out          [B, Hq, D]           double
+ *   probs        [B, Hq, max_blocks*bs] double or NULL: softmax weights,
+ *                zero past the context length
+ * A sequence with context length 0 gets an all-zero output row. */
+int oracle_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
+                             int64_t head_dim, int64_t block_size, int64_t num_blocks,
+                             int64_t max_blocks, int dtype, double scale, double *out,
+                             double *probs, int num_threads)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_blocks <= 0 || max_blocks <= 0 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_F16))
+        return ORACLE_ERR_ARG;
+    if (num_q_heads % num_kv_heads != 0)
+        return ORACLE_ERR_HEADS;
+    if (num_seqs == 0)
+        return ORACLE_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+        return ORACLE_ERR_ARG;
+
+    for (int64_t b = 0; b < num_seqs; ++b) {
+        const int64_t ctx = context_lens[b];
+        if (ctx < 0 || ctx > max_blocks * block_size)
+            return ORACLE_ERR_CTX;
+        const int64_t nblk = (ctx + block_size - 1) / block_size;
+        for (int64_t n = 0; n < nblk; ++n) {
+            const int64_t id = block_tables[b * max_blocks + n];
+            if (id < 0 || id >= num_blocks)
+                return ORACLE_ERR_BLOCK_RANGE;
+        }
+    }
+
+    const int64_t group = num_q_heads / num_kv_heads;
+    const int64_t max_tokens = max_blocks * block_size;
+    const int64_t pairs = num_seqs * num_q_heads;
+    int rc = ORACLE_OK;
+#ifdef _OPENMP
+    if (num_threads <= 0)
+        num_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads)
+#else
+    (void)num_threads;
+#endif
+    for (int64_t pair = 0; pair < pairs; ++pair) {
+        const int64_t b = pair / num_q_heads;
+        const int64_t h = pair % num_q_heads;
+        const int64_t g = h / group; /* KV head read by q head h */
+        const int64_t ctx = context_lens[b];
+        double *o = out + pair * head_dim;
+        double *p = probs ? probs + pair * max_tokens : NULL;
+        if (p)
+            memset(p, 0, sizeof(double) * (size_t)max_tokens);
+        if (ctx == 0) {
+            memset(o, 0, sizeof(double) * (size_t)head_dim);
+            continue;
+        }
+        double *s = (double *)malloc(sizeof(double) * (size_t)ctx);
+        if (!s) {
+            rc = ORACLE_ERR_ARG;
+            continue;
+        }
+        /* pass 1: scores s_t = scale * <q, K_t> and their maximum */
+        double m = -INFINITY;
+        for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t blk = block_tables[b * max_blocks + t / block_size];
+            const int64_t row = ((blk * num_kv_heads + g) * block_size + t % block_size) * head_dim;
+            double dot = 0.0;
+            for (int64_t j = 0; j < head_dim; ++j)
+                dot += widen(q, pair * head_dim + j, dtype) * widen(k_cache, row + j, dtype);
+            s[t] = scale * dot;
+            if (s[t] > m)
+                m = s[t];
+        }
+        /* pass 2: e_t = exp(s_t - m), l = sum e_t, o = sum e_t V_t / l */
+        double l = 0.0;
+        for (int64_t j = 0; j < head_dim; ++j)
+            o[j] = 0.0;
+        for (int64_t t = 0; t < ctx; ++t) {
+            const int64_t blk = block_tables[b * max_blocks + t / block_size];
+            const int64_t row = ((blk * num_kv_heads + g) * block_size + t % block_size) * head_dim;
+            const double e = exp(s[t] - m);
+            s[t] = e;
+            l += e;
+            for (int64_t j = 0; j < head_dim; ++j)
+                o[j] += e * widen(v_cache, row + j, dtype);
+        }
+        for (int64_t j = 0; j < head_dim; ++j)
+            o[j] /= l;
+        if (p)
+            for (int64_t t = 0; t < ctx; ++t)
+                p[t] = s[t] / l;
+        free(s);
+    }
+    return rc;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
