@@ -1,0 +1,234 @@
+"""Benchmark of the batched paged-attention decode step on one MI355X.
+
+One step is the whole hot path over one synthetic batch: for each of the
+workload's layers, the slot-mapped cache write of the batch's new tokens and
+the paged decode over the block tables (split-context kernel plus merge when
+partitions are used).  Inputs are generated once, copied to HBM, and stay
+resident; every layer owns its own K/V pool, so a 16-layer step touches about
+1.1 GB and the 256 MiB Infinity Cache cannot serve repeated reads.
+
+Printed: one JSON line.  ``value`` is whole-step throughput in algorithmic
+GB/s (bytes the method must move: valid K/V rows, q, out, table entries and
+lengths for the decode; k/v rows and slots for the write) per measured step
+time.  ``roofline`` describes the decode call (partition kernel, plus the
+merge kernel when the workload splits contexts), timed with HIP events
+recorded on the launch stream around every decode call inside the timed
+region.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
+the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama1b_b16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+import decode_inputs as di
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def decode_bytes(cfg: di.DecodeConfig, ctx: np.ndarray) -> int:
+    """Algorithmic bytes of one decode call: valid K/V rows, q, out, table entries, lengths."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    eb = cfg.elem_bytes
+    kv = int(ctx.sum()) * cfg.num_kv_heads * cfg.head_dim * eb * 2
+    qo = 2 * len(ctx) * cfg.num_q_heads * cfg.head_dim * eb
+    tables = int(di.blocks_needed(ctx, cfg.block_size).sum()) * 4
+    return kv + qo + tables + 4 * len(ctx)
+
+
+def write_bytes(cfg: di.DecodeConfig, num_tokens: int, num_written: int) -> int:
+    """Algorithmic bytes of one cache-write call: read k/v rows and slots, write the rows."""
+    row = cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+    return 2 * num_tokens * row + 2 * num_written * row + 4 * num_tokens
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama1b_b16", choices=sorted(di.CONFIGS))
+    ap.add_argument("--partition-tokens", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--min-step-gib", type=float, default=1.0,
+                    help="the workload's layers are replicated (fresh pools) until one step "
+                         "reads at least this much distinct K/V, so no layer is served from "
+                         "the 256 MiB Infinity Cache")
+    return ap.parse_args(argv)
+
+
+def cpu_baseline(cfg, lay, host_layers, budget_s: float):
+    """Time the fp64 oracle on whole layers of the workload until the budget is used."""
+    import oracle
+    threads = oracle.max_threads()
+    per_layer = decode_bytes(cfg, lay.context_lens)
+    done, t_total = 0, 0.0
+    while t_total < budget_s and done < 64:
+        t = host_layers[done % len(host_layers)]
+        t0 = time.perf_counter()
+        oracle.paged_attn_decode(t.q, t.k_cache, t.v_cache, lay.block_tables, lay.context_lens,
+                                 cfg.scale, num_threads=threads)
+        t_total += time.perf_counter() - t0
+        done += 1
+    return {
+        "value": round(per_layer * done / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} decode calls (whole layers, all {len(lay.context_lens)} sequences) of "
+                  f"the {cfg.name} workload, {t_total:.1f} s wall; cache write not included",
+        "ms_per_layer": round(t_total / done * 1e3, 3),
+    }
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every (sequence, KV head) pair is independent, see the sharding notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_attention_decode_photon_amd as pa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    device = torch.device("cuda:0")
+    cfg = di.CONFIGS[args.workload]
+    lay = di.make_layout(cfg)
+    n_layers = max(cfg.layers, 1)
+    host_layers = [di.make_layer(cfg, lay, layer) for layer in range(n_layers)]
+    pool_bytes = 2 * host_layers[0].k_cache.nbytes * n_layers
+    copies = int(min(512 // n_layers, max(1, -(-int(args.min_step_gib * 2**30) // pool_bytes))))
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    tables, lens, slots = up(lay.block_tables), up(lay.context_lens), up(lay.slot_mapping)
+    layers = []
+    for _ in range(copies):
+        for t in host_layers:
+            layers.append({"q": up(t.q), "kc": up(t.k_cache), "vc": up(t.v_cache),
+                           "k": up(t.k_new), "v": up(t.v_new), "out": torch.empty_like(up(t.q))})
+    max_ctx = lay.max_context_len
+    desc = pa.decode_desc(layers[0]["q"], layers[0]["kc"], tables, max_ctx, args.partition_tokens)
+    part = pa.partition_tokens(desc)
+    ws_bytes = pa.workspace_bytes(desc)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+    sptr = stream.cuda_stream
+    kvd = pa.kv_desc(layers[0]["kc"])
+    lib = pa.lib
+    import ctypes
+    descref, kvref = ctypes.byref(desc), ctypes.byref(kvd)
+    T = lay.slot_mapping.shape[0]
+    scale = cfg.scale
+
+    def write(L):
+        pa.check(lib.photon_kv_cache_write(L["k"].data_ptr(), L["v"].data_ptr(), slots.data_ptr(),
+                                           T, L["kc"].data_ptr(), L["vc"].data_ptr(), kvref, sptr))
+
+    def decode(L):
+        pa.check(lib.photon_paged_attn_decode(L["q"].data_ptr(), L["kc"].data_ptr(),
+                                              L["vc"].data_ptr(), tables.data_ptr(),
+                                              lens.data_ptr(), scale, descref, L["out"].data_ptr(),
+                                              workspace.data_ptr(), ws_bytes, sptr))
+
+    n_events = len(layers) * args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+
+    for _ in range(args.warmup):
+        for L in layers:
+            write(L)
+            decode(L)
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    i = 0
+    for _ in range(args.steps):
+        for L in layers:
+            write(L)
+            ev_a[i].record(stream)
+            decode(L)
+            ev_b[i].record(stream)
+            i += 1
+    stop.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(stop) / args.steps
+    call_us = [a.elapsed_time(b) * 1e3 for a, b in zip(ev_a, ev_b)]
+    call_mean = statistics.fmean(call_us)
+    call_med = statistics.median(call_us)
+
+    per_decode = decode_bytes(cfg, lay.context_lens)
+    n_written = int((lay.slot_mapping >= 0).sum())
+    per_write = write_bytes(cfg, T, n_written)
+    step_bytes = len(layers) * (per_decode + per_write)
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    achieved = per_decode / (call_mean * 1e-6) / 1e9
+    tok_per_layer = len(lay.context_lens) / (step_ms * 1e-3 / len(layers))
+
+    result = {
+        "metric": "decode attention KV GB/s (% of HBM peak) + tokens/s per layer at batch 16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block pool)",
+        "config": {
+            "workload": cfg.name,
+            "batch": len(lay.context_lens),
+            "layers_per_step": len(layers),
+            "num_q_heads": cfg.num_q_heads,
+            "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim,
+            "block_size": cfg.block_size,
+            "kv_dtype": cfg.dtype,
+            "context_sum": int(lay.context_lens.sum()),
+            "context_max": max_ctx,
+            "partition_tokens": part,
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s_per_layer": round(tok_per_layer, 1),
+        "decode_call_us_mean": round(call_mean, 3),
+        "decode_call_us_median": round(call_med, 3),
+        "decode_gbps_event_timed": round(achieved, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "photon_paged_attn_decode call (partition kernel"
+                      + (" + merge kernel" if part < max_ctx else "") + ")",
+            "bytes_per_launch": per_decode,
+        },
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(cfg, lay, host_layers, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

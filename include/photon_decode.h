@@ -1,0 +1,178 @@
+/*
+ * photon_decode.h - C ABI of the MI355X (gfx950) batched paged-attention
+ * decode library.
+ *
+ * The operations are the two steps of a decode step that the PhotonInfer
+ * README describes:
+ *   - "Technical details -> Paged attention": a block-level KV cache, per
+ *     sequence cache offsets (here: block tables), and one kernel that writes
+ *     the K/V of many sequences at once (here: a per-token slot mapping);
+ *   - "GPU-optimised kernels": batched paged attention with a numerically
+ *     stable softmax.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or keeps a pointer past the call (the README's
+ *     "C++20 architecture" section asks for zero-copy views; these are they).
+ *   - Tensors are dense, row-major.  The K and V pools share one layout,
+ *     [num_blocks, num_kv_heads, block_size, head_dim]; the row of token
+ *     position t of sequence b under KV head g is
+ *     pool[block_tables[b][t / block_size]][g][t % block_size][:].
+ *   - A slot is physical_block * block_size + offset_in_block (int32).
+ *   - stream is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued asynchronously; PHOTON_OK means "validated and launched".  A
+ *     fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Errors are returned, never thrown (the README's "C++20 architecture"
+ *     section: errors propagate explicitly as values).  All argument checks
+ *     run before any HIP call, so they behave the same with or without a GPU.
+ *     On failure nothing is launched and photon_last_error_detail() returns a
+ *     message for the calling thread.
+ *   - Device-resident indices (slot_mapping, block_tables, context_lens) are
+ *     NOT range-checked by the kernels: out-of-range values are a caller
+ *     error and may fault the GPU.
+ *   - Functions hold no global state and may be called from several threads.
+ */
+#ifndef PHOTON_DECODE_H
+#define PHOTON_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PHOTON_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define PHOTON_API __attribute__((visibility("default")))
+#else
+#define PHOTON_API
+#endif
+
+typedef enum photon_status {
+    PHOTON_OK = 0,
+    PHOTON_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad enum */
+    PHOTON_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, block_size, group */
+    PHOTON_ERR_WORKSPACE = 3,   /* workspace smaller than photon_paged_attn_workspace_bytes */
+    PHOTON_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} photon_status;
+
+/* Storage type of q, the K/V pools, new K/V rows and the output.
+ * Scores, softmax and accumulation are always fp32. */
+typedef enum photon_dtype {
+    PHOTON_F32 = 0,
+    PHOTON_F16 = 1
+} photon_dtype;
+
+/* Shape of one KV block pool (K and V pools have the same shape). */
+typedef struct photon_kv_desc {
+    int32_t num_blocks;   /* physical blocks in each pool, > 0                  */
+    int32_t num_kv_heads; /* > 0                                                 */
+    int32_t block_size;   /* tokens per block; 16 is built                      */
+    int32_t head_dim;     /* 64 or 128 are built                                */
+    int32_t dtype;        /* photon_dtype                                       */
+} photon_kv_desc;
+
+/* Shape of one decode call. */
+typedef struct photon_decode_desc {
+    int32_t num_seqs;           /* B, >= 0                                       */
+    int32_t num_q_heads;        /* Hq, a multiple of kv.num_kv_heads; the group
+                                   Hq / Hkv must be 1, 2, 4 or 8                 */
+    int32_t max_blocks_per_seq; /* row length of block_tables, > 0               */
+    int32_t max_context_len;    /* >= every context_lens[b], and
+                                   <= max_blocks_per_seq * block_size; sizes the
+                                   grid and the workspace                        */
+    int32_t partition_tokens;   /* 0 = choose automatically; otherwise tokens per
+                                   split-context partition, a positive multiple
+                                   of photon_paged_attn_partition_quantum()      */
+    photon_kv_desc kv;
+} photon_decode_desc;
+
+/*
+ * Slot-mapped KV cache write (README "Technical details -> Paged attention":
+ * one kernel writes K/V rows of many sequences).
+ *
+ * For every token i < num_tokens with slot_mapping[i] >= 0 and every KV head
+ * h, copies the raw bytes of k[i][h][:] into
+ * k_cache[slot / block_size][h][slot % block_size][:], and the same for v.
+ * Tokens whose slot is negative are skipped (padding).  No conversion: k, v
+ * and the pools share kv->dtype, and the copy is bit-exact.
+ *
+ *   k, v          [num_tokens, num_kv_heads, head_dim]   kv->dtype, 16-byte aligned
+ *   slot_mapping  [num_tokens] int32, each >= 0 slot distinct and
+ *                 < num_blocks * block_size (two tokens with one slot: the
+ *                 stored row is unspecified)
+ *   k_cache, v_cache  pools, updated in place, 16-byte aligned
+ *
+ * num_tokens == 0 launches nothing and returns PHOTON_OK.
+ */
+PHOTON_API photon_status photon_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
+                                    int32_t num_tokens, void *k_cache, void *v_cache,
+                                    const photon_kv_desc *kv, void *stream);
+
+/*
+ * Token granularity of partition_tokens: the number of tokens one wavefront
+ * of the decode kernel consumes per step for this shape.  Returns 0 and sets
+ * the detail message if desc is invalid or unsupported.
+ */
+PHOTON_API int32_t photon_paged_attn_partition_quantum(const photon_decode_desc *desc);
+
+/*
+ * Partition size a call with this descriptor will use (resolves
+ * partition_tokens == 0).  Returns 0 if desc is invalid or unsupported.
+ * When it is >= max_context_len the call runs a single pass and needs no
+ * workspace.
+ */
+PHOTON_API int32_t photon_paged_attn_partition_tokens(const photon_decode_desc *desc);
+
+/*
+ * Workspace bytes photon_paged_attn_decode needs for desc (0 for a single
+ * pass).  The workspace holds fp32 per-partition partial results
+ * (running maximum, exponential sum and unnormalised output rows); it is
+ * scratch, need not be initialised and is overwritten by every call.
+ */
+PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_desc *desc, size_t *bytes);
+
+/*
+ * Batched paged-attention decode with grouped-query heads (README "GPU-
+ * optimised kernels": batched paged attention, stable softmax).  For each
+ * sequence b and query head h, with g = h / (Hq / Hkv), ctx = context_lens[b]
+ * and K_t, V_t the rows of logical position t under KV head g:
+ *
+ *   s_t        = scale * <q[b][h], K_t>            for t < ctx
+ *   out[b][h]  = sum_t exp(s_t - max s) V_t / sum_t exp(s_t - max s)
+ *
+ * A sequence with ctx == 0 gets an all-zero row.  Table entries at or past
+ * ceil(ctx / block_size) and pool slots at or past ctx in the last block are
+ * never read.  When the partition size is below max_context_len the work is
+ * split over context partitions whose partial results are merged by a second
+ * kernel in a fixed order, so results are deterministic run to run.
+ *
+ *   q             [num_seqs, num_q_heads, head_dim]        kv.dtype, 16-byte aligned
+ *   k_cache, v_cache  pools (read only), 16-byte aligned
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32, entries < kv.num_blocks
+ *   context_lens  [num_seqs] int32, 0 <= ctx <= max_context_len
+ *   out           [num_seqs, num_q_heads, head_dim]        kv.dtype, 16-byte aligned
+ *   workspace     device scratch of workspace_bytes >= the size the workspace
+ *                 query returns, 16-byte aligned (may be NULL when that is 0)
+ */
+PHOTON_API photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                                       const int32_t *block_tables, const int32_t *context_lens,
+                                       float scale, const photon_decode_desc *desc, void *out,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static name of a status code. */
+PHOTON_API const char *photon_status_str(photon_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+PHOTON_API const char *photon_last_error_detail(void);
+
+/* PHOTON_ABI_VERSION of the loaded library. */
+PHOTON_API int32_t photon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PHOTON_DECODE_H */

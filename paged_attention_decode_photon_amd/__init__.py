@@ -1,0 +1,201 @@
+"""Python binding of the MI355X paged-attention decode library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libphoton_decode.so`` (built from ``csrc/`` by ``build.py``).
+Functions take torch tensors on a ROCm device, pass their data pointers and
+the current HIP stream through the C ABI declared in
+``include/photon_decode.h``, and raise :class:`PhotonError` on a non-OK
+status.  There is no fallback: if the library is missing, importing this
+package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libphoton_decode.so")
+
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_UNSUPPORTED = 2
+ERR_WORKSPACE = 3
+ERR_HIP = 4
+
+F32 = 0
+F16 = 1
+
+BLOCK_SIZE = 16
+
+
+class PhotonError(RuntimeError):
+    """A photon_* call returned a non-OK status."""
+
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}" if detail else name)
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+class KvDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("partition_tokens", ctypes.c_int32), ("kv", KvDesc)]
+
+
+def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m paged_attention_decode_photon_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    st = ctypes.c_int
+    lib.photon_kv_cache_write.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.POINTER(KvDesc), vp]
+    lib.photon_kv_cache_write.restype = st
+    lib.photon_paged_attn_partition_quantum.argtypes = [ctypes.POINTER(DecodeDesc)]
+    lib.photon_paged_attn_partition_quantum.restype = i32
+    lib.photon_paged_attn_partition_tokens.argtypes = [ctypes.POINTER(DecodeDesc)]
+    lib.photon_paged_attn_partition_tokens.restype = i32
+    lib.photon_paged_attn_workspace_bytes.argtypes = [ctypes.POINTER(DecodeDesc),
+                                                      ctypes.POINTER(sz)]
+    lib.photon_paged_attn_workspace_bytes.restype = st
+    lib.photon_paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float,
+                                             ctypes.POINTER(DecodeDesc), vp, vp, sz, vp]
+    lib.photon_paged_attn_decode.restype = st
+    lib.photon_status_str.argtypes = [st]
+    lib.photon_status_str.restype = ctypes.c_char_p
+    lib.photon_last_error_detail.argtypes = []
+    lib.photon_last_error_detail.restype = ctypes.c_char_p
+    lib.photon_abi_version.argtypes = []
+    lib.photon_abi_version.restype = i32
+    return lib
+
+
+lib = _load_library()
+
+
+def check(status: int) -> None:
+    if status != OK:
+        raise PhotonError(status, lib.photon_status_str(status).decode(),
+                          lib.photon_last_error_detail().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", f"dtype {t.dtype} not supported")
+
+
+def _stream_ptr(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _contig(name: str, t) -> None:
+    if not t.is_contiguous():
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", f"{name} is not contiguous")
+
+
+def kv_desc(k_cache) -> KvDesc:
+    nb, hkv, bs, d = k_cache.shape
+    return KvDesc(nb, hkv, bs, d, _dtype_code(k_cache))
+
+
+def decode_desc(q, k_cache, block_tables, max_context_len: int,
+                partition_tokens: int = 0) -> DecodeDesc:
+    b, hq, _ = q.shape
+    return DecodeDesc(b, hq, block_tables.shape[1], int(max_context_len), int(partition_tokens),
+                      kv_desc(k_cache))
+
+
+def kv_cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
+    """Write k[i], v[i] ([T, Hkv, D]) into pool slot ``slot_mapping[i]`` (in place)."""
+    for name, t in (("k", k), ("v", v), ("slot_mapping", slot_mapping), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _contig(name, t)
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "k, v and pools differ in dtype")
+    _, hkv, _, d = k_cache.shape
+    if tuple(k.shape) != (slot_mapping.shape[0], hkv, d) or k.shape != v.shape \
+            or v_cache.shape != k_cache.shape:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
+    desc = kv_desc(k_cache)
+    check(lib.photon_kv_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                    slot_mapping.shape[0], k_cache.data_ptr(), v_cache.data_ptr(),
+                                    ctypes.byref(desc), _stream_ptr(k_cache)))
+
+
+def partition_quantum(desc: DecodeDesc) -> int:
+    n = lib.photon_paged_attn_partition_quantum(ctypes.byref(desc))
+    if n == 0:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          lib.photon_last_error_detail().decode())
+    return n
+
+
+def partition_tokens(desc: DecodeDesc) -> int:
+    n = lib.photon_paged_attn_partition_tokens(ctypes.byref(desc))
+    if n == 0:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          lib.photon_last_error_detail().decode())
+    return n
+
+
+def workspace_bytes(desc: DecodeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    check(lib.photon_paged_attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                      max_context_len: int | None = None, out=None, workspace=None,
+                      partition_tokens: int = 0):
+    """GQA paged decode: out[b, h] = softmax(scale q K^T) V over context_lens[b] tokens.
+
+    q, out: [B, Hq, D]; pools: [NB, Hkv, 16, D]; block_tables: [B, max_blocks]
+    int32; context_lens: [B] int32.  ``max_context_len`` must bound every
+    context length (if None it is read back from the device, which
+    synchronises).  ``workspace`` (uint8 device tensor) is allocated through
+    torch when not given and needed.
+    """
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("context_lens", context_lens)):
+        _contig(name, t)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          "block_tables and context_lens must be int32")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q and pools differ")
+    if q.shape[2] != k_cache.shape[3] or block_tables.shape[0] != q.shape[0] \
+            or tuple(context_lens.shape) != (q.shape[0],):
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if context_lens.numel() else 0
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens)
+    ws_need = workspace_bytes(desc)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _contig("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape or dtype")
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.photon_paged_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       block_tables.data_ptr(), context_lens.data_ptr(),
+                                       float(scale), ctypes.byref(desc), out.data_ptr(), ws_ptr,
+                                       ws_len, _stream_ptr(q)))
+    return out

@@ -1,0 +1,256 @@
+// C ABI of the decode library: argument validation, partition sizing,
+// workspace sizing and launches.  Declarations and the contract of every
+// entry point are in include/photon_decode.h.
+//
+// Every check runs before the first HIP call, so invalid arguments return
+// the same status with or without a GPU, and nothing is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+#include "photon_decode.h"
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+photon_status fail(photon_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+photon_status ok()
+{
+    g_detail[0] = '\0';
+    return PHOTON_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int elem_bytes_of(int32_t dtype) { return dtype == PHOTON_F32 ? 4 : dtype == PHOTON_F16 ? 2 : 0; }
+
+// Auto partitioning: double the partition from one token per wave-step per
+// wave until the grid holds at most about four workgroups per compute unit of
+// an MI355X (256 CUs), capped so one workgroup never walks a very long span.
+constexpr int64_t kTargetWorkgroups = 4 * 256;
+constexpr int kMaxAutoPartition = 1024;
+
+photon_status check_kv(const photon_kv_desc *kv)
+{
+    if (!kv)
+        return fail(PHOTON_ERR_INVALID_ARG, "kv descriptor is NULL");
+    if (kv->num_blocks <= 0 || kv->num_kv_heads <= 0 || kv->block_size <= 0 || kv->head_dim <= 0)
+        return fail(PHOTON_ERR_INVALID_ARG,
+                    "kv sizes must be positive (num_blocks=%d num_kv_heads=%d block_size=%d "
+                    "head_dim=%d)",
+                    kv->num_blocks, kv->num_kv_heads, kv->block_size, kv->head_dim);
+    if (elem_bytes_of(kv->dtype) == 0)
+        return fail(PHOTON_ERR_INVALID_ARG, "unknown dtype %d", kv->dtype);
+    if ((int64_t)kv->num_blocks * kv->block_size > INT32_MAX)
+        return fail(PHOTON_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
+    if (kv->block_size != photon::kBlockTokens)
+        return fail(PHOTON_ERR_UNSUPPORTED, "block_size %d not built (16 is)", kv->block_size);
+    if (kv->head_dim != 64 && kv->head_dim != 128)
+        return fail(PHOTON_ERR_UNSUPPORTED, "head_dim %d not built (64, 128 are)", kv->head_dim);
+    if (kv->num_kv_heads > 65535)
+        return fail(PHOTON_ERR_UNSUPPORTED, "num_kv_heads %d above the grid limit", kv->num_kv_heads);
+    return PHOTON_OK;
+}
+
+struct Plan {
+    int group;
+    int elem_bytes;
+    int quantum;
+    int part_tokens;
+    int max_parts;
+    size_t ml_bytes;
+    size_t ws_bytes;
+};
+
+photon_status plan_decode(const photon_decode_desc *d, Plan *plan)
+{
+    if (!d)
+        return fail(PHOTON_ERR_INVALID_ARG, "decode descriptor is NULL");
+    photon_status st = check_kv(&d->kv);
+    if (st != PHOTON_OK)
+        return st;
+    if (d->num_seqs < 0 || d->num_q_heads <= 0 || d->max_blocks_per_seq <= 0 ||
+        d->max_context_len < 0 || d->partition_tokens < 0)
+        return fail(PHOTON_ERR_INVALID_ARG,
+                    "bad sizes (num_seqs=%d num_q_heads=%d max_blocks_per_seq=%d "
+                    "max_context_len=%d partition_tokens=%d)",
+                    d->num_seqs, d->num_q_heads, d->max_blocks_per_seq, d->max_context_len,
+                    d->partition_tokens);
+    if (d->num_q_heads % d->kv.num_kv_heads != 0)
+        return fail(PHOTON_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    d->num_q_heads, d->kv.num_kv_heads);
+    if ((int64_t)d->max_context_len > (int64_t)d->max_blocks_per_seq * d->kv.block_size)
+        return fail(PHOTON_ERR_INVALID_ARG,
+                    "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
+                    d->max_context_len, (long long)d->max_blocks_per_seq * d->kv.block_size);
+    const int group = d->num_q_heads / d->kv.num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return fail(PHOTON_ERR_UNSUPPORTED, "query heads per KV head %d not built (1, 2, 4, 8 are)",
+                    group);
+    if (d->num_seqs > 65535)
+        return fail(PHOTON_ERR_UNSUPPORTED, "num_seqs %d above the grid limit", d->num_seqs);
+
+    Plan p{};
+    p.group = group;
+    p.elem_bytes = elem_bytes_of(d->kv.dtype);
+    p.quantum = photon::decode_chunk_tokens(p.elem_bytes, d->kv.head_dim, group);
+    if (d->partition_tokens > 0) {
+        if (d->partition_tokens % p.quantum != 0)
+            return fail(PHOTON_ERR_INVALID_ARG, "partition_tokens %d is not a multiple of %d",
+                        d->partition_tokens, p.quantum);
+        p.part_tokens = d->partition_tokens;
+    } else {
+        const int64_t pairs = (int64_t)d->num_seqs * d->kv.num_kv_heads;
+        int part = photon::kDecodeWaves * p.quantum;
+        while (part < kMaxAutoPartition &&
+               pairs * ((d->max_context_len + part - 1) / part) > kTargetWorkgroups)
+            part *= 2;
+        p.part_tokens = part;
+    }
+    const int64_t parts = ((int64_t)d->max_context_len + p.part_tokens - 1) / p.part_tokens;
+    p.max_parts = parts < 1 ? 1 : (int)parts;
+    if (p.max_parts > 1) {
+        const size_t rows = (size_t)d->num_seqs * d->num_q_heads * p.max_parts;
+        p.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
+        p.ws_bytes = p.ml_bytes + rows * d->kv.head_dim * sizeof(float);
+    }
+    *plan = p;
+    return PHOTON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+photon_status photon_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
+                                    int32_t num_tokens, void *k_cache, void *v_cache,
+                                    const photon_kv_desc *kv, void *stream)
+{
+    photon_status st = check_kv(kv);
+    if (st != PHOTON_OK)
+        return st;
+    if (num_tokens < 0)
+        return fail(PHOTON_ERR_INVALID_ARG, "num_tokens %d is negative", num_tokens);
+    if (num_tokens == 0)
+        return ok();
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+        return fail(PHOTON_ERR_INVALID_ARG, "NULL data pointer");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PHOTON_ERR_INVALID_ARG, "k, v and the pools must be 16-byte aligned");
+    if (!aligned4(slot_mapping))
+        return fail(PHOTON_ERR_INVALID_ARG, "slot_mapping must be 4-byte aligned");
+    const int row_bytes = kv->head_dim * elem_bytes_of(kv->dtype);
+    hipError_t err = photon::launch_kv_cache_write(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                                   kv->num_kv_heads, kv->block_size, row_bytes,
+                                                   (hipStream_t)stream);
+    if (err != hipSuccess)
+        return fail(PHOTON_ERR_HIP, "kv cache write launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
+int32_t photon_paged_attn_partition_quantum(const photon_decode_desc *desc)
+{
+    Plan p;
+    return plan_decode(desc, &p) == PHOTON_OK ? p.quantum : 0;
+}
+
+int32_t photon_paged_attn_partition_tokens(const photon_decode_desc *desc)
+{
+    Plan p;
+    return plan_decode(desc, &p) == PHOTON_OK ? p.part_tokens : 0;
+}
+
+photon_status photon_paged_attn_workspace_bytes(const photon_decode_desc *desc, size_t *bytes)
+{
+    if (!bytes)
+        return fail(PHOTON_ERR_INVALID_ARG, "bytes is NULL");
+    Plan p;
+    photon_status st = plan_decode(desc, &p);
+    if (st != PHOTON_OK)
+        return st;
+    *bytes = p.ws_bytes;
+    return ok();
+}
+
+photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                                       const int32_t *block_tables, const int32_t *context_lens,
+                                       float scale, const photon_decode_desc *desc, void *out,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    Plan p;
+    photon_status st = plan_decode(desc, &p);
+    if (st != PHOTON_OK)
+        return st;
+    if (desc->num_seqs == 0)
+        return ok();
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+        return fail(PHOTON_ERR_INVALID_ARG, "NULL data pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PHOTON_ERR_INVALID_ARG, "q, the pools and out must be 16-byte aligned");
+    if (!aligned4(block_tables) || !aligned4(context_lens))
+        return fail(PHOTON_ERR_INVALID_ARG, "block_tables and context_lens must be 4-byte aligned");
+    if (!std::isfinite(scale))
+        return fail(PHOTON_ERR_INVALID_ARG, "scale is not finite");
+    if (workspace_bytes < p.ws_bytes)
+        return fail(PHOTON_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    p.ws_bytes);
+    if (p.ws_bytes > 0 && (!workspace || !aligned16(workspace)))
+        return fail(PHOTON_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
+
+    photon::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.ws_ml = p.ws_bytes ? static_cast<float *>(workspace) : nullptr;
+    a.ws_o = p.ws_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ml_bytes)
+                        : nullptr;
+    a.num_seqs = desc->num_seqs;
+    a.num_kv_heads = desc->kv.num_kv_heads;
+    a.group = p.group;
+    a.head_dim = desc->kv.head_dim;
+    a.elem_bytes = p.elem_bytes;
+    a.max_blocks = desc->max_blocks_per_seq;
+    a.part_tokens = p.part_tokens;
+    a.max_parts = p.max_parts;
+    a.qscale = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    hipError_t err = photon::launch_paged_decode(a, (hipStream_t)stream);
+    if (err != hipSuccess)
+        return fail(PHOTON_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
+const char *photon_status_str(photon_status status)
+{
+    switch (status) {
+    case PHOTON_OK: return "PHOTON_OK";
+    case PHOTON_ERR_INVALID_ARG: return "PHOTON_ERR_INVALID_ARG";
+    case PHOTON_ERR_UNSUPPORTED: return "PHOTON_ERR_UNSUPPORTED";
+    case PHOTON_ERR_WORKSPACE: return "PHOTON_ERR_WORKSPACE";
+    case PHOTON_ERR_HIP: return "PHOTON_ERR_HIP";
+    }
+    return "PHOTON_UNKNOWN_STATUS";
+}
+
+const char *photon_last_error_detail(void) { return g_detail; }
+
+int32_t photon_abi_version(void) { return PHOTON_ABI_VERSION; }
+
+}  // extern "C"

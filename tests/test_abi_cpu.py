@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: exported symbols and argument validation.
+
+Every call here fails validation (or has nothing to launch), which the
+library guarantees happens before its first HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_attention_decode_photon_amd as pa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "photon_decode.h")
+FAKE = 0x10000  # aligned, never dereferenced: each call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"PHOTON_API\s+[\w\s\*]+?\b(photon_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    assert {"photon_kv_cache_write", "photon_paged_attn_decode",
+            "photon_paged_attn_workspace_bytes", "photon_status_str"} <= names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_every_declared_symbol(name):
+    assert hasattr(pa.lib, name)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define PHOTON_ABI_VERSION (\d+)", open(HEADER).read())
+    assert pa.lib.photon_abi_version() == int(m.group(1))
+
+
+def test_status_names():
+    for code, name in [(0, "PHOTON_OK"), (1, "PHOTON_ERR_INVALID_ARG"),
+                       (2, "PHOTON_ERR_UNSUPPORTED"), (3, "PHOTON_ERR_WORKSPACE"),
+                       (4, "PHOTON_ERR_HIP")]:
+        assert pa.lib.photon_status_str(code).decode() == name
+
+
+def kv(nb=64, hkv=8, bs=16, d=64, dtype=pa.F32):
+    return pa.KvDesc(nb, hkv, bs, d, dtype)
+
+
+def dd(b=16, hq=32, mb=128, maxctx=2048, part=0, **kw):
+    return pa.DecodeDesc(b, hq, mb, maxctx, part, kv(**kw))
+
+
+def write(desc, n=4, k=FAKE, v=FAKE, slots=FAKE, kc=FAKE, vc=FAKE):
+    return pa.lib.photon_kv_cache_write(k, v, slots, n, kc, vc,
+                                        ctypes.byref(desc) if desc is not None else None, None)
+
+
+def detail():
+    return pa.lib.photon_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("desc,code", [
+    (None, pa.ERR_INVALID_ARG),
+    (kv(nb=0), pa.ERR_INVALID_ARG),
+    (kv(hkv=-1), pa.ERR_INVALID_ARG),
+    (kv(dtype=7), pa.ERR_INVALID_ARG),
+    (kv(bs=8), pa.ERR_UNSUPPORTED),
+    (kv(d=96), pa.ERR_UNSUPPORTED),
+    (kv(nb=1 << 28, bs=16), pa.ERR_INVALID_ARG),  # slots overflow int32
+])
+def test_cache_write_rejects_bad_descriptor(desc, code):
+    assert write(desc) == code
+    assert detail()
+
+
+def test_cache_write_rejects_bad_pointers():
+    assert write(kv(), k=None) == pa.ERR_INVALID_ARG
+    assert write(kv(), slots=None) == pa.ERR_INVALID_ARG
+    assert write(kv(), kc=FAKE + 8) == pa.ERR_INVALID_ARG   # pool not 16-byte aligned
+    assert write(kv(), slots=FAKE + 2) == pa.ERR_INVALID_ARG
+    assert write(kv(), n=-1) == pa.ERR_INVALID_ARG
+
+
+def test_cache_write_with_no_tokens_launches_nothing():
+    assert write(kv(), n=0, k=None, v=None, slots=None, kc=None, vc=None) == pa.OK
+
+
+def test_partition_quantum_and_auto_size():
+    # fp32 / d64 / group 4: two 16-token blocks per wave step
+    assert pa.lib.photon_paged_attn_partition_quantum(ctypes.byref(dd())) == 32
+    # group 8 with fp32 rows: one block per step keeps the partial scores in registers
+    assert pa.lib.photon_paged_attn_partition_quantum(ctypes.byref(dd(hq=64))) == 16
+    # fp16 / d128 / group 2
+    assert pa.lib.photon_paged_attn_partition_quantum(
+        ctypes.byref(dd(hq=16, d=128, dtype=pa.F16))) == 32
+    p = pa.lib.photon_paged_attn_partition_tokens(ctypes.byref(dd()))
+    assert p > 0 and p % 32 == 0
+    assert pa.lib.photon_paged_attn_partition_tokens(ctypes.byref(dd(part=96))) == 96
+
+
+def test_workspace_size_formula():
+    d = dd(b=3, hq=8, mb=40, maxctx=640, part=64, hkv=2)
+    parts = 10
+    ml = (3 * 8 * parts * 2 * 4 + 255) // 256 * 256
+    assert pa.workspace_bytes(d) == ml + 3 * 8 * parts * 64 * 4
+    # a single partition needs no workspace
+    assert pa.workspace_bytes(dd(b=3, hq=8, mb=40, maxctx=640, part=640, hkv=2)) == 0
+
+
+@pytest.mark.parametrize("desc,code", [
+    (dd(hq=30), pa.ERR_INVALID_ARG),            # Hq not a multiple of Hkv
+    (dd(hq=128), pa.ERR_UNSUPPORTED),           # group 16
+    (dd(hq=24), pa.ERR_UNSUPPORTED),            # group 3
+    (dd(maxctx=128 * 16 + 1), pa.ERR_INVALID_ARG),
+    (dd(maxctx=-1), pa.ERR_INVALID_ARG),
+    (dd(part=48), pa.ERR_INVALID_ARG),          # not a multiple of the quantum
+    (dd(part=-32), pa.ERR_INVALID_ARG),
+    (dd(b=-1), pa.ERR_INVALID_ARG),
+    (dd(b=70000), pa.ERR_UNSUPPORTED),
+    (dd(bs=32), pa.ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_descriptor(desc, code):
+    n = ctypes.c_size_t(0)
+    assert pa.lib.photon_paged_attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == code
+    assert _decode(desc) == code
+    assert detail()
+
+
+def _decode(desc, q=FAKE, kc=FAKE, vc=FAKE, tables=FAKE, lens=FAKE, scale=0.125, out=FAKE,
+            ws=FAKE, ws_bytes=1 << 30):
+    return pa.lib.photon_paged_attn_decode(q, kc, vc, tables, lens, scale,
+                                           ctypes.byref(desc) if desc is not None else None,
+                                           out, ws, ws_bytes, None)
+
+
+def test_decode_rejects_bad_pointers_scale_and_workspace():
+    d = dd(part=256)
+    need = pa.workspace_bytes(d)
+    assert need > 0
+    assert _decode(None) == pa.ERR_INVALID_ARG
+    assert _decode(d, q=None) == pa.ERR_INVALID_ARG
+    assert _decode(d, out=FAKE + 4) == pa.ERR_INVALID_ARG
+    assert _decode(d, tables=FAKE + 1) == pa.ERR_INVALID_ARG
+    assert _decode(d, scale=float("nan")) == pa.ERR_INVALID_ARG
+    assert _decode(d, scale=float("inf")) == pa.ERR_INVALID_ARG
+    assert _decode(d, ws_bytes=need - 1) == pa.ERR_WORKSPACE
+    assert _decode(d, ws=None, ws_bytes=need) == pa.ERR_INVALID_ARG
+    assert _decode(d, ws=FAKE + 8, ws_bytes=need) == pa.ERR_INVALID_ARG
+
+
+def test_decode_with_no_sequences_launches_nothing():
+    assert _decode(dd(b=0), q=None, kc=None, vc=None, tables=None, lens=None, out=None,
+                   ws=None, ws_bytes=0) == pa.OK

@@ -1,0 +1,237 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Tolerances (max-abs on every output element): 1e-4 for fp32 storage and
+2e-3 for fp16 storage with fp32 accumulation.  Cache writes must be
+bit-exact over the whole pool.  The oracle runs first on every input set,
+so its precondition checks (slot and block-id ranges, context bounds) guard
+each launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_inputs as di
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {np.dtype(np.float32): 1e-4, np.dtype(np.float16): 2e-3}
+
+
+@pytest.fixture(scope="module")
+def pa():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import paged_attention_decode_photon_amd as mod
+    return mod
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def gpu_decode(pa, q, kc, vc, tables, ctx, scale, max_ctx=None, part=0):
+    out = pa.paged_attn_decode(dev(q), dev(kc), dev(vc), dev(tables), dev(ctx), scale,
+                               max_context_len=int(ctx.max()) if max_ctx is None else max_ctx,
+                               partition_tokens=part)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def assert_close(got, ref, dtype, what=""):
+    err = np.abs(got.astype(np.float64) - ref)
+    worst = float(np.nanmax(err)) if err.size else 0.0
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert worst <= TOL[np.dtype(dtype)], f"{what}: max-abs error {worst:.3e}"
+    return worst
+
+
+def random_case(rng, dtype, b, hq, hkv, d, ctx_list=None, max_ctx=64, spare=3):
+    ctx = np.array(ctx_list, np.int32) if ctx_list is not None else \
+        rng.integers(0, max_ctx + 1, b).astype(np.int32)
+    b = len(ctx)
+    need = (ctx.astype(np.int64) + 15) // 16
+    nb = int(need.sum()) + spare
+    mb = max(int(need.max()), 1)
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((b, mb), -1, np.int32)
+    p = 0
+    for i, n in enumerate(need):
+        tables[i, :n] = perm[p:p + n]
+        p += n
+    q = rng.standard_normal((b, hq, d)).astype(dtype)
+    kc = rng.standard_normal((nb, hkv, 16, d)).astype(dtype)
+    vc = rng.standard_normal((nb, hkv, 16, d)).astype(dtype)
+    return q, kc, vc, tables, ctx
+
+
+# ----------------------------------------------------------------- cache write
+
+@pytest.mark.parametrize("dtype,hkv,d", [(np.float32, 8, 64), (np.float16, 8, 64),
+                                         (np.float16, 8, 128), (np.float32, 2, 128)])
+def test_cache_write_bit_exact(pa, dtype, hkv, d):
+    rng = np.random.default_rng(20)
+    nb, t = 300, 77
+    kc = rng.standard_normal((nb, hkv, 16, d)).astype(dtype)
+    vc = rng.standard_normal((nb, hkv, 16, d)).astype(dtype)
+    k = rng.standard_normal((t, hkv, d)).astype(dtype)
+    v = rng.standard_normal((t, hkv, d)).astype(dtype)
+    if dtype == np.float16:  # NaN payloads, infinities and subnormals must survive
+        k.view(np.uint16)[0, 0, :8] = [0x7E01, 0xFC00, 0x0001, 0x8001, 0x7C00, 0x7D55, 0xFFFF, 0x03FF]
+    slots = di.random_injective_slots(nb, 16, t, rng, pad_fraction=0.15)
+    ek, ev = oracle.kv_cache_write(k, v, slots, kc, vc)
+    gk, gv = dev(kc), dev(vc)
+    pa.kv_cache_write(dev(k), dev(v), dev(slots), gk, gv)
+    torch.cuda.synchronize()
+    assert host(gk).tobytes() == ek.tobytes()
+    assert host(gv).tobytes() == ev.tobytes()
+
+
+def test_cache_write_all_padding_is_noop(pa):
+    rng = np.random.default_rng(21)
+    kc = rng.standard_normal((4, 2, 16, 64)).astype(np.float32)
+    gk, gv = dev(kc), dev(kc)
+    k = dev(np.ones((5, 2, 64), np.float32))
+    pa.kv_cache_write(k, k, dev(np.full(5, -1, np.int32)), gk, gv)
+    torch.cuda.synchronize()
+    assert host(gk).tobytes() == kc.tobytes() and host(gv).tobytes() == kc.tobytes()
+
+
+# ------------------------------------------------------------ decode vs oracle
+
+@pytest.mark.parametrize("name,layer", [("tiny", 0), ("llama1b_b1", 0), ("llama1b_b16", 0),
+                                        ("llama1b_b16", 11), ("cb_b64", 0)])
+def test_decode_matches_oracle_on_workloads(pa, name, layer):
+    cfg = di.CONFIGS[name]
+    lay = di.make_layout(cfg)
+    t = di.make_layer(cfg, lay, layer)
+    ref = oracle.paged_attn_decode(t.q, t.k_cache, t.v_cache, lay.block_tables,
+                                   lay.context_lens, cfg.scale)
+    got = gpu_decode(pa, t.q, t.k_cache, t.v_cache, lay.block_tables, lay.context_lens, cfg.scale)
+    err = assert_close(got, ref, cfg.np_dtype, name)
+    print(f"{name} layer {layer}: max-abs {err:.3e}")
+
+
+def test_decode_qwen3_long_sampled(pa):
+    # Full size (8 x 32768 tokens, fp16, d128); the oracle computes two sequences.
+    cfg = di.CONFIGS["qwen3_long"]
+    lay = di.make_layout(cfg)
+    t = di.make_layer(cfg, lay)
+    got = gpu_decode(pa, t.q, t.k_cache, t.v_cache, lay.block_tables, lay.context_lens, cfg.scale)
+    for b in (0, 5):
+        ref = oracle.paged_attn_decode(t.q[b:b + 1], t.k_cache, t.v_cache,
+                                       lay.block_tables[b:b + 1], lay.context_lens[b:b + 1],
+                                       cfg.scale)
+        err = assert_close(got[b:b + 1], ref, cfg.np_dtype, f"qwen3_long seq {b}")
+        print(f"qwen3_long seq {b}: max-abs {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "cb_b64"])
+def test_decode_step_writes_then_attends(pa, name):
+    # The step writes each sequence's new K/V at logical position ctx-1 and
+    # then attends over all ctx tokens, the new one included.
+    cfg = di.CONFIGS[name]
+    lay = di.make_layout(cfg)
+    t = di.make_layer(cfg, lay)
+    ek, ev = oracle.kv_cache_write(t.k_new, t.v_new, lay.slot_mapping, t.k_cache, t.v_cache)
+    ref = oracle.paged_attn_decode(t.q, ek, ev, lay.block_tables, lay.context_lens, cfg.scale)
+    gk, gv = dev(t.k_cache), dev(t.v_cache)
+    pa.kv_cache_write(dev(t.k_new), dev(t.v_new), dev(lay.slot_mapping), gk, gv)
+    out = pa.paged_attn_decode(dev(t.q), gk, gv, dev(lay.block_tables), dev(lay.context_lens),
+                               cfg.scale, max_context_len=lay.max_context_len)
+    torch.cuda.synchronize()
+    assert host(gk).tobytes() == ek.tobytes() and host(gv).tobytes() == ev.tobytes()
+    assert_close(host(out), ref, cfg.np_dtype, name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "cb_b64"])
+def test_unread_slots_never_reach_the_output(pa, name):
+    cfg = di.CONFIGS[name]
+    lay = di.make_layout(cfg, num_blocks=None)
+    t = di.make_layer(cfg, lay)
+    args = (lay.block_tables, lay.context_lens, cfg.scale)
+    clean = gpu_decode(pa, t.q, t.k_cache, t.v_cache, *args)
+    kp = di.poison_unused(cfg, lay, t.k_cache)
+    vp = di.poison_unused(cfg, lay, t.v_cache)
+    poisoned = gpu_decode(pa, t.q, kp, vp, *args)
+    assert np.isfinite(poisoned).all()
+    assert poisoned.tobytes() == clean.tobytes()
+
+
+def test_block_permutation_and_repeat_are_bit_identical(pa):
+    rng = np.random.default_rng(22)
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 12, 32, 8, 64, max_ctx=700, spare=20)
+    base = gpu_decode(pa, q, kc, vc, tables, ctx, 0.125, part=128)
+    again = gpu_decode(pa, q, kc, vc, tables, ctx, 0.125, part=128)
+    assert base.tobytes() == again.tobytes()
+    pi = rng.permutation(kc.shape[0])
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[pi], vc2[pi] = kc, vc
+    t2 = np.where(tables >= 0, pi[np.maximum(tables, 0)], -1).astype(np.int32)
+    perm = gpu_decode(pa, q, kc2, vc2, t2, ctx, 0.125, part=128)
+    assert perm.tobytes() == base.tobytes()
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [(np.float32, 32, 8, 64), (np.float16, 32, 8, 64),
+                                            (np.float16, 16, 8, 128)])
+def test_partition_sizes_agree_with_oracle(pa, dtype, hq, hkv, d):
+    rng = np.random.default_rng(23)
+    q, kc, vc, tables, ctx = random_case(rng, dtype, 6, hq, hkv, d,
+                                         ctx_list=[1, 17, 255, 256, 257, 1100])
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.11)
+    desc = pa.decode_desc(dev(q), dev(kc), dev(tables), int(ctx.max()))
+    qu = pa.partition_quantum(desc)
+    for part in sorted({qu, 2 * qu, 4 * qu, 128, 256, 512, 2048}):
+        if part % qu:
+            continue
+        got = gpu_decode(pa, q, kc, vc, tables, ctx, 0.11, part=part)
+        assert_close(got, ref, dtype, f"partition {part}")
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_every_built_shape(pa, dtype, d, group):
+    rng = np.random.default_rng(1000 + group * 10 + d + (dtype == np.float16))
+    hkv = 2
+    ctx = [0, 1, 15, 16, 17, 31, 33, 64, 100, 333]
+    q, kc, vc, tables, ctx = random_case(rng, dtype, len(ctx), hkv * group, hkv, d, ctx_list=ctx)
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, float(np.float32(d ** -0.5)))
+    for part in (0, 64):
+        got = gpu_decode(pa, q, kc, vc, tables, ctx, float(np.float32(d ** -0.5)), part=part)
+        assert_close(got, ref, dtype, f"G{group} d{d} part {part}")
+        assert (got[0] == 0).all()  # empty context -> zero row
+
+
+def test_context_edges_around_partition_boundaries(pa):
+    rng = np.random.default_rng(24)
+    ctx = [0, 1, 2, 15, 16, 17, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1000]
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 0, 32, 8, 64, ctx_list=ctx)
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    for part in (0, 128, 256, 512):
+        got = gpu_decode(pa, q, kc, vc, tables, ctx, 0.125, part=part)
+        assert_close(got, ref, np.float32, f"partition {part}")
+
+
+def test_max_context_len_may_exceed_every_context(pa):
+    rng = np.random.default_rng(25)
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 5, 8, 2, 64, max_ctx=90)
+    tables = np.concatenate([tables, np.full((5, 20), -1, np.int32)], axis=1)
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    got = gpu_decode(pa, q, kc, vc, tables, ctx, 0.125, max_ctx=tables.shape[1] * 16)
+    assert_close(got, ref, np.float32, "loose max_context_len")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 4.0, 40.0])
+def test_large_and_negative_scores(pa, scale):
+    # scale 40 puts scores in the hundreds: exp only stays finite after the
+    # running maximum is subtracted.
+    rng = np.random.default_rng(26)
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 4, 8, 2, 64, ctx_list=[5, 70, 300, 31])
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, scale)
+    for part in (0, 64):
+        got = gpu_decode(pa, q, kc, vc, tables, ctx, scale, part=part)
+        assert_close(got, ref, np.float32, f"scale {scale}")
