@@ -7,6 +7,11 @@ the current HIP stream through the C ABI declared in
 ``include/photon_decode.h``, and raise :class:`PhotonError` on a non-OK
 status.  There is no fallback: if the library is missing, importing this
 package raises.
+
+The library must run inside the same HIP runtime as PyTorch (it uses torch's
+streams and allocations), so torch is imported before the library is loaded:
+the dynamic loader then binds the library's ``libamdhip64.so.7`` dependency
+to the copy torch already mapped.  Import fails if two runtimes end up mapped.
 """
 from __future__ import annotations
 
@@ -50,11 +55,25 @@ class DecodeDesc(ctypes.Structure):
                 ("partition_tokens", ctypes.c_int32), ("kv", KvDesc)]
 
 
+def _hip_runtimes_mapped() -> set[str]:
+    try:
+        with open("/proc/self/maps") as f:
+            return {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:
+        return set()
+
+
 def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    import torch  # noqa: F401  (maps torch's HIP runtime first; see module docstring)
+
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           "`python -m paged_attention_decode_photon_amd.build`")
     lib = ctypes.CDLL(path)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped ({sorted(runtimes)}); the decode library "
+                          "must share PyTorch's")
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     st = ctypes.c_int
     lib.photon_kv_cache_write.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.POINTER(KvDesc), vp]

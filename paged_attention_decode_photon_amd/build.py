@@ -3,7 +3,9 @@
     python -m paged_attention_decode_photon_amd.build [--jobs N]
 
 Each HIP source is compiled to an object in parallel, then linked into a
-shared library next to this file.  Packed-fp32 VALU forms are disabled for
+shared library next to this file.  Code objects use version 5, which every
+ROCm 7 runtime loads (the library runs inside the HIP runtime that PyTorch
+ships, which may be older than this hipcc).  Packed-fp32 VALU forms are disabled for
 all device code (-packed-fp32-ops): the kernels rely on scalar fp32 FMA only.
 """
 from __future__ import annotations
@@ -25,7 +27,7 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
+    f"--offload-arch={ARCH}", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
@@ -52,7 +54,7 @@ def build(jobs: int | None = None) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
-    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     return LIB
 

@@ -81,9 +81,12 @@ template <>
 struct Elem<_Float16> {
     __device__ static void unpack(const u32x4 &v, float (&f)[8])
     {
+        // Copy each dword out of the vector before the bit cast: a bit cast of
+        // the vector element itself reads the vector's first dword.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            half2_t h = __builtin_bit_cast(half2_t, v[i]);
+            const uint32_t word = v[i];
+            half2_t h = __builtin_bit_cast(half2_t, word);
             f[2 * i] = (float)h[0];
             f[2 * i + 1] = (float)h[1];
         }
