@@ -2,18 +2,17 @@
 
 One step is the whole hot path over one synthetic batch: for each of the
 workload's layers, the slot-mapped cache write of the batch's new tokens and
-the paged decode over the block tables (split-context kernel plus merge when
-partitions are used).  Inputs are generated once, copied to HBM, and stay
+the paged decode over the block tables (one kernel; split contexts merge
+inside it).  Inputs are generated once, copied to HBM, and stay
 resident; every layer owns its own K/V pool, so a 16-layer step touches about
 1.1 GB and the 256 MiB Infinity Cache cannot serve repeated reads.
 
 Printed: one JSON line.  ``value`` is whole-step throughput in algorithmic
 GB/s (bytes the method must move: valid K/V rows, q, out, table entries and
 lengths for the decode; k/v rows and slots for the write) per measured step
-time.  ``roofline`` describes the decode call (partition kernel, plus the
-merge kernel when the workload splits contexts), timed with HIP events
-recorded on the launch stream around every decode call inside the timed
-region.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
+time.  ``roofline`` describes the decode kernel (one launch per decode call;
+split contexts merge inside it), timed with HIP events recorded on the
+launch stream around every decode call inside the timed region.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
 the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama1b_b16]
@@ -125,7 +124,7 @@ def main(argv=None) -> int:
     desc = pa.decode_desc(layers[0]["q"], layers[0]["kc"], tables, max_ctx, args.partition_tokens)
     part = pa.partition_tokens(desc)
     ws_bytes = pa.workspace_bytes(desc)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device)
+    workspace = pa.new_workspace(ws_bytes, device)
     stream = torch.cuda.current_stream(device)
     sptr = stream.cuda_stream
     kvd = pa.kv_desc(layers[0]["kc"])
@@ -219,8 +218,7 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None,
-            "kernel": "photon_paged_attn_decode call (partition kernel"
-                      + (" + merge kernel" if part < max_ctx else "") + ")",
+            "kernel": "paged_decode_partition (one launch per photon_paged_attn_decode call)",
             "bytes_per_launch": per_decode,
         },
     }

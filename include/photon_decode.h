@@ -83,9 +83,14 @@ typedef struct photon_decode_desc {
     int32_t max_context_len;    /* >= every context_lens[b], and
                                    <= max_blocks_per_seq * block_size; sizes the
                                    grid and the workspace                        */
-    int32_t partition_tokens;   /* 0 = choose automatically; otherwise tokens per
-                                   split-context partition, a positive multiple
-                                   of photon_paged_attn_partition_quantum()      */
+    int32_t partition_tokens;   /* 0 = automatic (enough wavefronts for about
+                                   64 KiB of K/V reads in flight per CU);
+                                   otherwise the most tokens one wavefront
+                                   handles when every sequence is at
+                                   max_context_len, a positive multiple of
+                                   photon_paged_attn_partition_quantum(); the
+                                   actual batch is always split evenly over
+                                   the wavefronts this implies                   */
     photon_kv_desc kv;
 } photon_decode_desc;
 
@@ -112,25 +117,31 @@ PHOTON_API photon_status photon_kv_cache_write(const void *k, const void *v, con
                                     const photon_kv_desc *kv, void *stream);
 
 /*
- * Token granularity of partition_tokens: the number of tokens one wavefront
- * of the decode kernel consumes per step for this shape.  Returns 0 and sets
- * the detail message if desc is invalid or unsupported.
+ * Token granularity of partition_tokens: the tokens of one unit of work (a
+ * chunk of whole KV blocks of one sequence and KV head) for this shape.
+ * Returns 0 and sets the detail message if desc is invalid or unsupported.
  */
 PHOTON_API int32_t photon_paged_attn_partition_quantum(const photon_decode_desc *desc);
 
 /*
- * Partition size a call with this descriptor will use (resolves
- * partition_tokens == 0).  Returns 0 if desc is invalid or unsupported.
- * When it is >= max_context_len the call runs a single pass and needs no
- * workspace.
+ * Tokens per wavefront a call with this descriptor will use for the largest
+ * batch it allows (resolves partition_tokens == 0).  Returns 0 if desc is
+ * invalid or unsupported.
  */
 PHOTON_API int32_t photon_paged_attn_partition_tokens(const photon_decode_desc *desc);
 
 /*
- * Workspace bytes photon_paged_attn_decode needs for desc (0 for a single
- * pass).  The workspace holds fp32 per-partition partial results
- * (running maximum, exponential sum and unnormalised output rows); it is
- * scratch, need not be initialised and is overwritten by every call.
+ * Workspace bytes photon_paged_attn_decode needs for desc (0 only when
+ * num_seqs is 0).  Layout: one int32 arrival counter per (sequence, KV head),
+ * then two fp32 partial records per wavefront (running maximum and
+ * exponential sum of each query head of a group, then their unnormalised
+ * output rows).
+ *
+ * The workspace must be zero-filled once before its first use (for example
+ * allocated with torch.zeros or cleared with hipMemset).  Every call that
+ * completes leaves the counters at zero again, so the same workspace serves
+ * later calls of any shape without clearing.  Calls that may run at the same
+ * time (other streams) need workspaces of their own.
  */
 PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_desc *desc, size_t *bytes);
 
@@ -145,9 +156,11 @@ PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_d
  *
  * A sequence with ctx == 0 gets an all-zero row.  Table entries at or past
  * ceil(ctx / block_size) and pool slots at or past ctx in the last block are
- * never read.  When the partition size is below max_context_len the work is
- * split over context partitions whose partial results are merged by a second
- * kernel in a fixed order, so results are deterministic run to run.
+ * never read.  One kernel is launched: it splits the batch's K/V reads
+ * evenly over its wavefronts, whatever the mix of context lengths; a
+ * (sequence, KV head) split over several wavefronts is merged by the last of
+ * them to finish, in a fixed order, so results are deterministic run to run.
+ * num_seqs is at most 2048 (PHOTON_ERR_UNSUPPORTED above).
  *
  *   q             [num_seqs, num_q_heads, head_dim]        kv.dtype, 16-byte aligned
  *   k_cache, v_cache  pools (read only), 16-byte aligned
@@ -155,7 +168,8 @@ PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_d
  *   context_lens  [num_seqs] int32, 0 <= ctx <= max_context_len
  *   out           [num_seqs, num_q_heads, head_dim]        kv.dtype, 16-byte aligned
  *   workspace     device scratch of workspace_bytes >= the size the workspace
- *                 query returns, 16-byte aligned (may be NULL when that is 0)
+ *                 query returns, 16-byte aligned, zero-filled before its first
+ *                 use
  */
 PHOTON_API photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                                        const int32_t *block_tables, const int32_t *context_lens,

@@ -176,6 +176,12 @@ def workspace_bytes(desc: DecodeDesc) -> int:
     return n.value
 
 
+def new_workspace(nbytes: int, device):
+    """Zero-filled workspace tensor (the counters in it must start at zero)."""
+    import torch
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
                       max_context_len: int | None = None, out=None, workspace=None,
                       partition_tokens: int = 0):
@@ -184,8 +190,8 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
     q, out: [B, Hq, D]; pools: [NB, Hkv, 16, D]; block_tables: [B, max_blocks]
     int32; context_lens: [B] int32.  ``max_context_len`` must bound every
     context length (if None it is read back from the device, which
-    synchronises).  ``workspace`` (uint8 device tensor) is allocated through
-    torch when not given and needed.
+    synchronises).  ``workspace`` (uint8 device tensor from
+    :func:`new_workspace`) is allocated through torch when not given and needed.
     """
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
@@ -210,7 +216,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
         if out.shape != q.shape or out.dtype != q.dtype:
             raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape or dtype")
     if ws_need and workspace is None:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(ws_need, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(lib.photon_paged_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),

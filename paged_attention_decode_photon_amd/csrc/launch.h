@@ -8,15 +8,31 @@
 
 namespace photon {
 
+// Build-time tuning knobs of the decode kernel (defaults are the tuned values).
+#ifndef PHOTON_DECODE_WAVES
+#define PHOTON_DECODE_WAVES 4    // wavefronts per decode workgroup
+#endif
+#ifndef PHOTON_DECODE_PREFETCH
+#define PHOTON_DECODE_PREFETCH 0 // 1: load the next chunk before consuming the current one
+#endif
+#ifndef PHOTON_KV_LOAD_AUX
+#define PHOTON_KV_LOAD_AUX 0     // cache-policy bits of the K/V buffer loads
+#endif
+#ifndef PHOTON_DECODE_CHUNK_BLOCKS
+#define PHOTON_DECODE_CHUNK_BLOCKS 0  // KV blocks per unit of work; 0: shape rule below
+#endif
+
 constexpr int kBlockTokens = 16;     // tokens per KV block the decode kernels are built for
-constexpr int kDecodeWaves = 4;      // wavefronts per decode workgroup
+constexpr int kDecodeWaves = PHOTON_DECODE_WAVES;
 
 // KV blocks one decode wavefront loads per loop step.  Two blocks while the
 // per-lane partial scores stay at <= 32 registers and a row is <= 256 bytes,
 // else one.
 constexpr int decode_chunk_blocks(int elem_bytes, int head_dim, int group)
 {
-    return (head_dim * elem_bytes <= 256 && (head_dim * elem_bytes / 64) * group <= 16) ? 2 : 1;
+    return PHOTON_DECODE_CHUNK_BLOCKS > 0 ? PHOTON_DECODE_CHUNK_BLOCKS
+           : (head_dim * elem_bytes <= 256 && (head_dim * elem_bytes / 64) * group <= 16) ? 2
+                                                                                           : 1;
 }
 
 // Tokens one decode wavefront handles per loop step (the partition quantum).
@@ -25,6 +41,17 @@ constexpr int decode_chunk_tokens(int elem_bytes, int head_dim, int group)
     return decode_chunk_blocks(elem_bytes, head_dim, group) * kBlockTokens;
 }
 
+// Floats of one partial record: the unnormalised output rows of the group's
+// query heads, then the running max and the exponential sum of each; padded
+// to a multiple of four floats.
+constexpr int decode_record_floats(int head_dim, int group)
+{
+    return (2 * group + group * head_dim + 3) & ~3;
+}
+
+// Sequences per call: the decode kernel keeps per-sequence prefix sums in LDS.
+constexpr int kMaxDecodeSeqs = 2048;
+
 struct DecodeArgs {
     const void *q;
     const void *k_cache;
@@ -32,20 +59,19 @@ struct DecodeArgs {
     const int32_t *block_tables;
     const int32_t *context_lens;
     void *out;
-    float *ws_ml;  // [B][Hq][max_parts][2] (running max in log2 units, exp sum)
-    float *ws_o;   // [B][Hq][max_parts][D] unnormalised partial outputs
+    int *ws_count;  // [B][Hkv] units merged so far per segment; zero between calls
+    float *ws_rec;  // [num_waves][2] partial records of decode_record_floats each
     int num_seqs;
     int num_kv_heads;
     int group;
     int head_dim;
     int elem_bytes;
     int max_blocks;
-    int part_tokens;
-    int max_parts;
-    float qscale;  // scale * log2(e)
+    int num_waves;  // wavefronts launched; a multiple of kDecodeWaves
+    float qscale;   // scale * log2(e)
 };
 
-// Partition kernel (and, when max_parts > 1, the merge kernel) on stream.
+// One decode launch on stream (partitions merge inside the same kernel).
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
 
 hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slots,

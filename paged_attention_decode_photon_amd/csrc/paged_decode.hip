@@ -1,5 +1,4 @@
-// Batched paged-attention decode for gfx950: split-context partition kernel
-// and the kernel that merges partitions.
+// Batched paged-attention decode for gfx950 (CDNA4), one kernel per call.
 //
 // Operation (PhotonInfer README, "GPU-optimised kernels": batched paged
 // attention with a stable softmax; "Technical details -> Paged attention":
@@ -8,16 +7,37 @@
 //   out[b][h] = sum_t exp(s_t - m) V_t / sum_t exp(s_t - m),
 //   s_t = scale * <q[b][h], K_t>,  m = max_t s_t,  t < context_lens[b].
 //
-// Work decomposition.  One workgroup of kDecodeWaves wavefronts owns one
-// (context partition p, KV head g, sequence b) and all G query heads that
-// read KV head g, so every K/V byte is fetched from HBM exactly once.  A
-// wavefront walks its partition in chunks of U blocks (CT = 16 U tokens).
+// Work decomposition (balanced split of the whole batch).  A "segment" is one
+// (sequence b, KV head g) pair together with the G query heads that read it,
+// so every K/V byte is fetched from HBM once.  A segment is cut into chunks
+// of CT = 16 U tokens; the chunks of all segments, sequence-major then
+// KV-head-major, form one list of U_tot units.  The kernel launches NW
+// wavefronts and wave s takes units [s U_tot / NW, (s+1) U_tot / NW) (NW is
+// capped at U_tot, so no slice is empty): every
+// wave gets the same number of bytes to read however ragged the contexts
+// are, which keeps all compute units streaming until the end.  Context
+// lengths live on the device, so each workgroup first forms the prefix sum
+// of per-sequence unit counts in LDS and every wave finds its first unit by
+// binary search.
+//
+// A wave's slice covers pieces of one or more segments.  A piece that holds
+// a whole segment writes its normalised output directly.  Otherwise the
+// piece's (max, sum, unnormalised rows) go to a workspace record and the
+// wave adds the piece's unit count to the segment's arrival counter; the
+// wave that completes the count merges all pieces of the segment in slice
+// order (deterministic whichever wave that is) and resets the counter to
+// zero.  Waves of one segment may run on different XCDs, whose L2 caches are
+// not coherent with each other; rather than agent-scope fences (an L2
+// write-back or invalidate, far too slow here) only the partial results
+// travel coherently, as agent-scope atomic stores and loads, and a wave waits
+// for its stores to complete before it counts its arrival.  No workgroup
+// barrier is used after the prefix sum: waves never wait for each other.
 //
 // Lane layout.  A K/V row is RB = D * sizeof(T) bytes, i.e. L = RB / 16
 // lanes of one 16-byte load each; one wave-wide load covers RPI = 64 / L
 // rows and a 16-token block takes NIB = 16 / RPI loads.  Lane (r, c) with
-// r = lane / L, c = lane % L always holds byte chunk c of some row; each 16
-// bytes a quad of lanes loads are contiguous.
+// r = lane / L, c = lane % L always holds byte chunk c of some row; the 16
+// bytes of each quad of lanes are contiguous.
 //
 // Scores without select-heavy reductions.  Per chunk a lane forms NS = NU*G
 // partial dot products (NU = U*NIB loads, G heads), each over its own chunk
@@ -38,10 +58,7 @@
 //
 // Softmax.  Scores are kept in log2 units (q is pre-multiplied by
 // scale * log2 e) and use v_exp_f32.  Each wave keeps an online maximum and
-// sum per head; the waves of a workgroup are merged through LDS.  When the
-// sequence has one partition the workgroup writes the normalised output,
-// otherwise (max, sum, unnormalised row) go to the workspace and
-// paged_decode_merge combines partitions in index order.
+// sum per head over its piece.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -58,6 +75,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // Fourth descriptor word of a raw (unswizzled, stride 0) buffer on gfx9-family.
 constexpr int kRawBufferWord3 = 0x00020000;
 
+
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
@@ -73,7 +91,11 @@ struct Elem<float> {
         f[2] = __uint_as_float(v[2]);
         f[3] = __uint_as_float(v[3]);
     }
-    __device__ static float to_float(float x) { return x; }
+    __device__ static u32x4 pack(const float (&f)[4])
+    {
+        return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                     __float_as_uint(f[3])};
+    }
     __device__ static float from_float(float x) { return x; }
 };
 
@@ -91,7 +113,19 @@ struct Elem<_Float16> {
             f[2 * i + 1] = (float)h[1];
         }
     }
-    __device__ static float to_float(_Float16 x) { return (float)x; }
+    __device__ static u32x4 pack(const float (&f)[8])
+    {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            half2_t h;
+            h[0] = (_Float16)f[2 * i];
+            h[1] = (_Float16)f[2 * i + 1];
+            const uint32_t word = __builtin_bit_cast(uint32_t, h);
+            v[i] = word;
+        }
+        return v;
+    }
     __device__ static _Float16 from_float(float x) { return (_Float16)x; }
 };
 
@@ -111,10 +145,34 @@ struct Shape {
     static constexpr int NS = NU * G;                 // partial-score slots
     static constexpr int CP = cmin(LOG2G + ilog2(NIB), LOG2L);  // reduce-scatter steps
     static constexpr int NK = NS >> CP;               // scores per lane after the butterfly
+    static constexpr int REC = decode_record_floats(D, G);  // floats per partial record
     static_assert(L * E == D, "row split");
     static_assert(L >= G && L >= 8 && L <= 32, "lane layout");
     static_assert(CT == decode_chunk_tokens(EB, D, G), "chunk size");
 };
+
+// Partial records travel between waves that may sit on different XCDs,
+// whose L2 caches are not coherent with each other.  They are written and
+// read with device-scope (sc1) buffer accesses, which write through and read
+// past the per-XCD L2, so no cache-wide fence is needed.
+constexpr int kDeviceScope = 16;  // cache-policy bits: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(float *rec, int floats)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(rec, (short)0, floats * 4, kRawBufferWord3);
+}
+// Wait until every vector memory operation this wave issued has completed
+// (stores included); the memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void wait_vector_memory()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// Compiler-only barrier for memory accesses.
+__device__ __forceinline__ void compiler_memory_barrier()
+{
+    asm volatile("" ::: "memory");
+}
 
 // Mask of the reduce-scatter step that halves slot bit k.  The mask has bit
 // k set and no higher bit, so it maps live slots onto live slots.
@@ -135,110 +193,152 @@ __device__ __forceinline__ void reduce_scatter(float (&part)[NS])
     }
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(
-    const T *__restrict__ q, const T *__restrict__ k_cache, const T *__restrict__ v_cache,
-    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    T *__restrict__ out, float *__restrict__ ws_ml, float *__restrict__ ws_o, int num_kv_heads,
-    int max_blocks, int part_tokens, int max_parts, float qscale)
+struct KernelArgs {
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    void *out;
+    int *ws_count;
+    float *ws_rec;
+    int num_seqs;
+    int num_kv_heads;
+    int max_blocks;
+    int num_waves;
+    float qscale;
+};
+
+// First unit of slice s (slices split [0, total) as evenly as integers allow).
+__device__ __forceinline__ int slice_start(int s, int total, int nw)
 {
+    return (int)(((long long)s * total) / nw);
+}
+// Slice that holds unit u: the largest s with slice_start(s) <= u.
+__device__ __forceinline__ int slice_of(int u, int total, int nw)
+{
+    return (int)((((long long)u + 1) * nw - 1) / total);
+}
+
+template <typename T, int D, int G>
+struct WaveDecoder {
     using S = Shape<T, D, G>;
-    constexpr int E = S::E, L = S::L, RPI = S::RPI, NIB = S::NIB, CT = S::CT, NU = S::NU;
-    constexpr int NS = S::NS, CP = S::CP, NK = S::NK, RB = S::RB;
-    constexpr int WAVES = kDecodeWaves;
+    static constexpr int E = S::E, L = S::L, RPI = S::RPI, NIB = S::NIB, CT = S::CT;
+    static constexpr int NU = S::NU, NS = S::NS, CP = S::CP, NK = S::NK, RB = S::RB;
 
-    __shared__ __attribute__((aligned(16))) float p_lds[WAVES][CT][G];
-    __shared__ float red_m[WAVES][G];
-    __shared__ float red_l[WAVES][G];
-    __shared__ __attribute__((aligned(16))) float red_o[WAVES][G][D];
-
-    const int p = blockIdx.x;
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
-    const int hq = num_kv_heads * G;
-    const int ctx = context_lens[b];
-    const int t0 = p * part_tokens;
-    T *out_rows = out + ((size_t)b * hq + (size_t)g * G) * D;
-
-    if (t0 >= ctx) {
-        if (p == 0) {  // empty context: the row is defined as zero
-            for (int i = threadIdx.x; i < G * D; i += WAVES * 64)
-                out_rows[i] = Elem<T>::from_float(0.0f);
-        }
-        return;
-    }
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nparts = (ctx + part_tokens - 1) / part_tokens;
-    const int tok_end = min(ctx, t0 + part_tokens);
-    const int nchunks = (tok_end - t0 + CT - 1) / CT;
-
-    const int c = lane & (L - 1);         // byte chunk of the row
-    const int r = lane >> S::LOG2L;       // row inside a wave-wide load
-    const int phi = c & ((1 << CP) - 1);  // slot permutation of this lane
-    const int row_x = phi >> S::LOG2G;    // load-index xor (stays inside a block)
-    const int head_x = phi & (G - 1);     // head xor
-    const int my_head = c & (G - 1);      // head of the scores this lane ends with
-
-    // q rows of the group, in this lane's head order, pre-scaled to log2 units.
-    float qf[G][E];
-#pragma unroll
-    for (int hs = 0; hs < G; ++hs) {
-        const T *row = q + ((size_t)b * hq + (size_t)g * G + (hs ^ head_x)) * D + c * E;
-        Elem<T>::unpack(*reinterpret_cast<const u32x4 *>(row), qf[hs]);
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            qf[hs][e] *= qscale;
-    }
-
+    const KernelArgs &a;
+    float (*p_lds)[G];  // this wave's [CT][G] softmax weights
+    int lane, c, r, phi, row_x, head_x, my_head;
     int k_off[NIB], v_off[NIB];
+
+    // state of the current piece
+    int b, g, ctx;
+    int nblk;      // blocks holding the sequence's context
+    int win0;      // first block index of the table window
+    int tbl_win;   // lane i: block_tables[b][win0 + i] (0 past the context)
+    float qf[G][E];
+    float m_run, l_run;
+    float o_acc[G][E];
+
+    __device__ WaveDecoder(const KernelArgs &args, float (*lds)[G]) : a(args), p_lds(lds)
+    {
+        lane = threadIdx.x & 63;
+        c = lane & (L - 1);
+        r = lane >> S::LOG2L;
+        phi = c & ((1 << CP) - 1);
+        row_x = phi >> S::LOG2G;
+        head_x = phi & (G - 1);
+        my_head = c & (G - 1);
 #pragma unroll
-    for (int i = 0; i < NIB; ++i) {
-        k_off[i] = (((i ^ row_x) * RPI + r) * RB) + c * 16;
-        v_off[i] = ((i * RPI + r) * RB) + c * 16;
+        for (int i = 0; i < NIB; ++i) {
+            k_off[i] = (((i ^ row_x) * RPI + r) * RB) + c * 16;
+            v_off[i] = ((i * RPI + r) * RB) + c * 16;
+        }
     }
 
-    float m_run = -INFINITY;  // running maximum (log2 units) of head my_head
-    float l_run = 0.0f;       // this lane's share of the exponential sum
-    float o_acc[G][E];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            o_acc[h][e] = 0.0f;
+    // Load 64 block-table entries starting at block n0, one per lane, so the
+    // K/V loads of the following units need no dependent table read.
+    __device__ void load_table_window(int n0)
+    {
+        win0 = n0;
+        const int n = n0 + lane;
+        tbl_win = n < nblk ? a.block_tables[(size_t)b * a.max_blocks + n] : 0;
+    }
 
-    const int32_t *table = block_tables + (size_t)b * max_blocks;
-    const size_t tile_stride = (size_t)kBlockTokens * RB;
+    // Make the window hold blocks [n_first, n_last] (n_last - n_first < 64).
+    // Called at the start of a step, before its K/V loads are issued: the
+    // wait for a refreshed window then never holds up loads in flight.
+    __device__ void cover_blocks(int n_first, int n_last)
+    {
+        if (n_last - win0 >= 64)
+            load_table_window(n_first);
+    }
 
-    for (int ch = wave; ch < nchunks; ch += WAVES) {
-        const int ct0 = t0 + ch * CT;
+    __device__ int block_at(int n) const { return __builtin_amdgcn_readlane(tbl_win, n - win0); }
+
+    __device__ void begin_piece(int b_, int g_, int ctx_, int ch0)
+    {
+        b = b_;
+        g = g_;
+        ctx = ctx_;
+        nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
+        load_table_window(ch0 * S::U);
+        const int hq = a.num_kv_heads * G;
+        const T *q = (const T *)a.q;
+#pragma unroll
+        for (int hs = 0; hs < G; ++hs) {
+            const T *row = q + ((size_t)b * hq + (size_t)g * G + (hs ^ head_x)) * D + c * E;
+            Elem<T>::unpack(*reinterpret_cast<const u32x4 *>(row), qf[hs]);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                qf[hs][e] *= a.qscale;
+        }
+        m_run = -INFINITY;
+        l_run = 0.0f;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                o_acc[h][e] = 0.0f;
+    }
+
+    // Issue the K and V loads of chunk ch (U blocks) of the current segment.
+    // With live == false every load gets an empty descriptor: it returns
+    // zeros without touching memory.
+    __device__ void load_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU], bool live = true) const
+    {
+        const size_t tile_stride = (size_t)kBlockTokens * RB;
         __amdgpu_buffer_rsrc_t rk[S::U], rv[S::U];
 #pragma unroll
         for (int u = 0; u < S::U; ++u) {
-            const int n = (ct0 / kBlockTokens) + u;
-            int rows = ctx - n * kBlockTokens;
+            const int n = ch * S::U + u;
+            int rows = live ? ctx - n * kBlockTokens : 0;
             rows = rows > kBlockTokens ? kBlockTokens : rows;
             int blk = 0;
             if (rows > 0)
-                blk = table[n];
+                blk = block_at(n);
             else
                 rows = 0;
-            const size_t tile = ((size_t)blk * num_kv_heads + g) * tile_stride;
-            rk[u] = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)k_cache + tile), (short)0,
-                                                      rows * RB, kRawBufferWord3);
-            rv[u] = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)v_cache + tile), (short)0,
-                                                      rows * RB, kRawBufferWord3);
+            const size_t tile = ((size_t)blk * a.num_kv_heads + g) * tile_stride;
+            rk[u] = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)a.k_cache + tile),
+                                                      (short)0, rows * RB, kRawBufferWord3);
+            rv[u] = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)a.v_cache + tile),
+                                                      (short)0, rows * RB, kRawBufferWord3);
         }
-
-        u32x4 kd[NU], vd[NU];
 #pragma unroll
         for (int i = 0; i < NU; ++i)
-            kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rk[i / NIB], k_off[i % NIB], 0, 0);
+            kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rk[i / NIB], k_off[i % NIB], 0,
+                                                          PHOTON_KV_LOAD_AUX);
 #pragma unroll
         for (int i = 0; i < NU; ++i)
-            vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rv[i / NIB], v_off[i % NIB], 0, 0);
+            vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rv[i / NIB], v_off[i % NIB], 0,
+                                                          PHOTON_KV_LOAD_AUX);
+    }
 
+    // Scores, online softmax update and P.V for chunk ch.
+    __device__ void consume_chunk(int ch, const u32x4 (&kd)[NU], const u32x4 (&vd)[NU])
+    {
+        const int ct0 = ch * CT;
         // Partial dot products over this lane's chunk: slot (i, hs) pairs the
         // lane's load i with query head hs ^ head_x.
         float part[NS];
@@ -269,7 +369,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(
             const int ld = item >> S::LOG2G;
             const int tok = (ld / NIB) * kBlockTokens + (ld % NIB) * RPI + r;
             s_tok[n] = tok;
-            v = (ct0 + tok < tok_end) ? v : -INFINITY;
+            v = (ct0 + tok < ctx) ? v : -INFINITY;
             s[n] = v;
             cmax = fmaxf(cmax, v);
         }
@@ -282,7 +382,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(
         for (int n = 0; n < NK; ++n) {
             const float pv = __builtin_amdgcn_exp2f(s[n] - m_new);
             psum += pv;
-            p_lds[wave][s_tok[n]][my_head] = pv;
+            p_lds[s_tok[n]][my_head] = pv;
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
@@ -311,7 +411,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(
             float pw[G];
 #pragma unroll
             for (int h = 0; h < G; ++h)
-                pw[h] = p_lds[wave][tok][h];
+                pw[h] = p_lds[tok][h];
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -323,102 +423,315 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // Per-wave totals.  Lanes that differ only in directly-summed row bits
-    // hold copies of the same scores; count each score once.
-    float l_once = ((c >> CP) == 0) ? l_run : 0.0f;
-    l_once = allreduce_bits<S::LOG2G, 6, OpSum>(l_once);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            o_acc[h][e] = allreduce_bits<S::LOG2L, 6, OpSum>(o_acc[h][e]);
-
-    if (lane < G) {
-        red_m[wave][lane] = m_run;
-        red_l[wave][lane] = l_once;
+    // Chunks [ch0, ch1) of the current segment.
+    __device__ void run_chunks(int ch0, int ch1)
+    {
+        if constexpr (PHOTON_DECODE_PREFETCH) {
+            // Two chunks per step, both loaded before the first is consumed.
+            // The code inside a step is straight-line, so the wait before
+            // each consume covers only that chunk's loads.
+            for (int ch = ch0; ch < ch1; ch += 2) {
+                const bool two = ch + 1 < ch1;
+                cover_blocks(ch * S::U, (ch + 2) * S::U - 1);
+                u32x4 ka[NU], va[NU], kb[NU], vb[NU];
+                load_chunk(ch, ka, va);
+                load_chunk(ch + 1, kb, vb, two);
+                consume_chunk(ch, ka, va);
+                if (two)
+                    consume_chunk(ch + 1, kb, vb);
+            }
+        } else {
+            for (int ch = ch0; ch < ch1; ++ch) {
+                cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
+                u32x4 kd[NU], vd[NU];
+                load_chunk(ch, kd, vd);
+                consume_chunk(ch, kd, vd);
+            }
+        }
     }
-    if (r == 0) {
+
+    // Reduce the piece's per-lane state to per-head totals: afterwards every
+    // lane holds the exponential sum of head my_head in l_run, and lanes with
+    // r == 0 hold the summed output rows for their chunk c of every head.
+    __device__ void reduce_piece()
+    {
+        // Lanes that differ only in directly-summed row bits hold copies of
+        // the same scores; count each score once.
+        const float l_once = ((c >> CP) == 0) ? l_run : 0.0f;
+        l_run = allreduce_bits<S::LOG2G, 6, OpSum>(l_once);
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                red_o[wave][h][c * E + e] = o_acc[h][e];
+                o_acc[h][e] = allreduce_bits<S::LOG2L, 6, OpSum>(o_acc[h][e]);
     }
-    __syncthreads();
 
-    for (int i = threadIdx.x; i < G * D; i += WAVES * 64) {
-        const int h = i / D;
-        const int dim = i % D;
-        float m = red_m[0][h];
+    __device__ T *out_rows() const
+    {
+        return (T *)a.out + ((size_t)b * a.num_kv_heads * G + (size_t)g * G) * D;
+    }
+
+    __device__ void write_output() const
+    {
+        T *dst = out_rows();
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w)
-            m = fmaxf(m, red_m[w][h]);
-        float lsum = 0.0f, o = 0.0f;
+        for (int h = 0; h < G; ++h) {
+            const float inv = 1.0f / read_lane(l_run, h);
+            if (r == 0) {
+                float v[E];
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const float f = __builtin_amdgcn_exp2f(red_m[w][h] - m);
-            lsum = __builtin_fmaf(f, red_l[w][h], lsum);
-            o = __builtin_fmaf(f, red_o[w][h][dim], o);
-        }
-        if (nparts == 1) {
-            out_rows[i] = Elem<T>::from_float(o / lsum);
-        } else {
-            const size_t slot = ((size_t)b * hq + (size_t)g * G + h) * max_parts + p;
-            ws_o[slot * D + dim] = o;
-            if (dim == 0) {
-                ws_ml[slot * 2] = m;
-                ws_ml[slot * 2 + 1] = lsum;
+                for (int e = 0; e < E; ++e)
+                    v[e] = o_acc[h][e] * inv;
+                *reinterpret_cast<u32x4 *>(dst + (size_t)h * D + c * E) = Elem<T>::pack(v);
             }
         }
     }
-}
 
-// Merge the partitions of every (sequence, query head) that has more than one:
-// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with M = max_p m_p,
-// accumulated in partition order.
-template <typename T, int D>
-__global__ __launch_bounds__(D) void paged_decode_merge(T *__restrict__ out,
-                                                         const float *__restrict__ ws_ml,
-                                                         const float *__restrict__ ws_o,
-                                                         const int32_t *__restrict__ context_lens,
-                                                         int num_q_heads, int part_tokens,
-                                                         int max_parts)
-{
-    const int h = blockIdx.x;
-    const int b = blockIdx.y;
-    const int dim = threadIdx.x;
-    const int ctx = context_lens[b];
-    const int nparts = (ctx + part_tokens - 1) / part_tokens;
-    if (nparts <= 1)
-        return;
-    const size_t base = ((size_t)b * num_q_heads + h) * max_parts;
-    const float *ml = ws_ml + base * 2;
-    float m = -INFINITY;
-    for (int i = 0; i < nparts; ++i)
-        m = fmaxf(m, ml[2 * i]);
-    float lsum = 0.0f, o = 0.0f;
-    for (int i = 0; i < nparts; ++i) {
-        const float f = __builtin_amdgcn_exp2f(ml[2 * i] - m);
-        lsum = __builtin_fmaf(f, ml[2 * i + 1], lsum);
-        o = __builtin_fmaf(f, ws_o[(base + i) * D + dim], o);
+    // Record layout (fp32): o[G][D] unnormalised rows, then m[G], then l[G];
+    // REC floats per record (a multiple of four).
+    __device__ void store_record(float *rec) const
+    {
+        const __amdgpu_buffer_rsrc_t rs = record_rsrc(rec, S::REC);
+        if (r == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int k = 0; k < E / 4; ++k) {
+                    const u32x4 v{__float_as_uint(o_acc[h][4 * k]),
+                                  __float_as_uint(o_acc[h][4 * k + 1]),
+                                  __float_as_uint(o_acc[h][4 * k + 2]),
+                                  __float_as_uint(o_acc[h][4 * k + 3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (h * D + c * E + 4 * k) * 4, 0,
+                                                           kDeviceScope);
+                }
+        }
+        if (lane < G) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), rs, (G * D + lane) * 4,
+                                                  0, kDeviceScope);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_run), rs,
+                                                  (G * D + G + lane) * 4, 0, kDeviceScope);
+        }
     }
-    out[((size_t)b * num_q_heads + h) * D + dim] = Elem<T>::from_float(o / lsum);
+
+    // Merge the records of every piece of segment (b, g), units [su0, su1),
+    // in slice order, and write the normalised output.  Each lane folds four
+    // consecutive outputs of one head; kBatch records are loaded at a time.
+    __device__ void merge_segment(int su0, int su1, int total, int nw) const
+    {
+        constexpr int kBatch = 8;
+        const int s_first = slice_of(su0, total, nw);
+        const int s_last = slice_of(su1 - 1, total, nw);
+        const int first_role = slice_start(s_first, total, nw) == su0 ? 0 : 1;
+        T *dst = out_rows();
+        compiler_memory_barrier();
+        for (int v = lane; v < G * D / 4; v += 64) {
+            const int i = 4 * v;  // first of this lane's four outputs
+            const int h = i / D;
+            float m = -INFINITY, lsum = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int s0 = s_first; s0 <= s_last; s0 += kBatch) {
+                float mj[kBatch], lj[kBatch];
+                u32x4 oj[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const int s = s0 + k;
+                    const bool in = s <= s_last;
+                    const int role = s == s_first ? first_role : 0;
+                    const __amdgpu_buffer_rsrc_t rs =
+                        record_rsrc(a.ws_rec + ((size_t)s * 2 + role) * S::REC, in ? S::REC : 0);
+                    oj[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 4, 0, kDeviceScope);
+                    mj[k] = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(rs, (G * D + h) * 4, 0, kDeviceScope));
+                    lj[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rs, (G * D + G + h) * 4, 0, kDeviceScope));
+                    if (!in)
+                        mj[k] = -INFINITY;
+                }
+                float m_new = m;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    m_new = fmaxf(m_new, mj[k]);
+                const float rescale = __builtin_amdgcn_exp2f(m - m_new);
+                lsum *= rescale;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] *= rescale;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const float f = __builtin_amdgcn_exp2f(mj[k] - m_new);
+                    lsum = __builtin_fmaf(f, lj[k], lsum);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = __builtin_fmaf(f, __uint_as_float(oj[k][e]), o[e]);
+                }
+                m = m_new;
+            }
+            const float inv = 1.0f / lsum;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dst[i + e] = Elem<T>::from_float(o[e] * inv);
+        }
+    }
+};
+
+// Inclusive prefix sum of one value per thread over the workgroup.
+__device__ int block_inclusive_scan(int v, int *wave_totals)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int n = __shfl_up(v, d, 64);
+        if (lane >= d)
+            v += n;
+    }
+    if (lane == 63)
+        wave_totals[wave] = v;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w)
+        before += wave_totals[w];
+    __syncthreads();
+    return v + before;
 }
 
 template <typename T, int D, int G>
-hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
+__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelArgs a)
 {
-    const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((paged_decode_partition<T, D, G>), grid, dim3(kDecodeWaves * 64), 0,
-                       stream, (const T *)a.q, (const T *)a.k_cache, (const T *)a.v_cache,
-                       a.block_tables, a.context_lens, (T *)a.out, a.ws_ml, a.ws_o,
-                       a.num_kv_heads, a.max_blocks, a.part_tokens, a.max_parts, a.qscale);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.max_parts <= 1)
-        return err;
-    hipLaunchKernelGGL((paged_decode_merge<T, D>), dim3(a.num_kv_heads * G, a.num_seqs), dim3(D),
-                       0, stream, (T *)a.out, a.ws_ml, a.ws_o, a.context_lens,
-                       a.num_kv_heads * G, a.part_tokens, a.max_parts);
+    using S = Shape<T, D, G>;
+    constexpr int CT = S::CT;
+    constexpr int WAVES = kDecodeWaves;
+    constexpr int NT = WAVES * 64;
+
+    __shared__ int unit_end[kMaxDecodeSeqs];  // inclusive prefix of units per sequence
+    __shared__ int ctx_lds[kMaxDecodeSeqs];
+    __shared__ int wave_totals[WAVES];
+    __shared__ __attribute__((aligned(16))) float p_lds[WAVES][CT][G];
+
+    const int B = a.num_seqs;
+    const int hkv = a.num_kv_heads;
+
+    // Units per sequence (Hkv * chunks) and their inclusive prefix sum.  Each
+    // thread owns a contiguous run of sequences.
+    const int per = (B + NT - 1) / NT;
+    const int first = threadIdx.x * per;
+    int mine = 0;
+    for (int j = 0; j < per; ++j) {
+        const int bb = first + j;
+        if (bb < B) {
+            const int cl = a.context_lens[bb];
+            ctx_lds[bb] = cl;
+            mine += hkv * ((cl + CT - 1) / CT);
+        }
+    }
+    int run = block_inclusive_scan(mine, wave_totals) - mine;
+    for (int j = 0; j < per; ++j) {
+        const int bb = first + j;
+        if (bb < B) {
+            run += hkv * ((ctx_lds[bb] + CT - 1) / CT);
+            unit_end[bb] = run;
+        }
+    }
+    __syncthreads();
+
+    // Values read from LDS are the same in every lane, but the compiler cannot
+    // know that; readfirstlane keeps everything derived from them in scalar
+    // registers (a divergent buffer descriptor would wrap each load in a
+    // waterfall loop).
+    const int total = __builtin_amdgcn_readfirstlane(unit_end[B - 1]);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int s = blockIdx.x * WAVES + wave;
+
+    // Sequences with an empty context have no units; their rows are zero.
+    for (int bb = s; bb < B; bb += a.num_waves) {
+        if (__builtin_amdgcn_readfirstlane(ctx_lds[bb]) == 0) {
+            T *row = (T *)a.out + (size_t)bb * hkv * G * D;
+            for (int i = lane; i < hkv * G * D; i += 64)
+                row[i] = Elem<T>::from_float(0.0f);
+        }
+    }
+    // Slices over min(waves, units) wavefronts are never empty, so every
+    // slice between two others holds a record of any segment spanning them.
+    const int nw = min(a.num_waves, total);
+    if (s >= nw)
+        return;
+    const int u_begin = slice_start(s, total, nw);
+    const int u_end = slice_start(s + 1, total, nw);
+
+    WaveDecoder<T, D, G> w(a, p_lds[wave]);
+
+    // First sequence whose units reach past u_begin.
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(unit_end[mid]) <= u_begin)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    int b = lo;
+    int u = u_begin;
+    while (u < u_end) {
+        const int seq_end = __builtin_amdgcn_readfirstlane(unit_end[b]);
+        const int ctx = __builtin_amdgcn_readfirstlane(ctx_lds[b]);
+        const int nch = (ctx + CT - 1) / CT;        // > 0: u lies inside sequence b
+        const int seq_begin = seq_end - hkv * nch;
+        const int g = (u - seq_begin) / nch;
+        const int seg_begin = seq_begin + g * nch;  // first unit of segment (b, g)
+        const int seg_end = seg_begin + nch;
+        const int piece_end = min(seg_end, u_end);
+        const int ch0 = u - seg_begin;
+        const int ch1 = piece_end - seg_begin;
+
+        w.begin_piece(b, g, ctx, ch0);
+        w.run_chunks(ch0, ch1);
+        w.reduce_piece();
+        if (ch0 == 0 && ch1 == nch) {
+            w.write_output();
+        } else {
+            const int role = (u == u_begin) ? 0 : 1;
+            w.store_record(a.ws_rec + ((size_t)s * 2 + role) * S::REC);
+            wait_vector_memory();
+            int done = 0;
+            if (lane == 0)
+                done = __hip_atomic_fetch_add(&a.ws_count[(size_t)b * hkv + g], ch1 - ch0,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            done = __builtin_amdgcn_readfirstlane(done) + (ch1 - ch0);
+            if (done == nch) {
+                w.merge_segment(seg_begin, seg_end, total, nw);
+                if (lane == 0)
+                    __hip_atomic_store(&a.ws_count[(size_t)b * hkv + g], 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        u = piece_end;
+        if (u == seq_end) {  // move on to the next sequence that has units
+            ++b;
+            while (b < B && __builtin_amdgcn_readfirstlane(unit_end[b]) == u)
+                ++b;
+        }
+    }
+}
+
+template <typename T, int D, int G>
+hipError_t launch_typed(const DecodeArgs &d, hipStream_t stream)
+{
+    KernelArgs a;
+    a.q = d.q;
+    a.k_cache = d.k_cache;
+    a.v_cache = d.v_cache;
+    a.block_tables = d.block_tables;
+    a.context_lens = d.context_lens;
+    a.out = d.out;
+    a.ws_count = d.ws_count;
+    a.ws_rec = d.ws_rec;
+    a.num_seqs = d.num_seqs;
+    a.num_kv_heads = d.num_kv_heads;
+    a.max_blocks = d.max_blocks;
+    a.num_waves = d.num_waves;
+    a.qscale = d.qscale;
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, G>), dim3(d.num_waves / kDecodeWaves),
+                       dim3(kDecodeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 

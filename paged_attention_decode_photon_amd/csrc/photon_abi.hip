@@ -39,11 +39,15 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 int elem_bytes_of(int32_t dtype) { return dtype == PHOTON_F32 ? 4 : dtype == PHOTON_F16 ? 2 : 0; }
 
-// Auto partitioning: double the partition from one token per wave-step per
-// wave until the grid holds at most about four workgroups per compute unit of
-// an MI355X (256 CUs), capped so one workgroup never walks a very long span.
-constexpr int64_t kTargetWorkgroups = 4 * 256;
-constexpr int kMaxAutoPartition = 1024;
+// Default number of decode wavefronts: enough per compute unit of an MI355X
+// (256 CUs) that the units being read, one per wave, add up to 64 KiB in
+// flight per CU, and at least four.  Each wave takes an equal share of the
+// batch's units.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kBytesInFlightPerCu = 64 * 1024;
+constexpr int64_t kMinWavesPerCu = 4;
+// Upper bound on wavefronts, which bounds the workspace.
+constexpr int64_t kMaxWaves = 1 << 20;
 
 photon_status check_kv(const photon_kv_desc *kv)
 {
@@ -70,12 +74,14 @@ photon_status check_kv(const photon_kv_desc *kv)
 struct Plan {
     int group;
     int elem_bytes;
-    int quantum;
-    int part_tokens;
-    int max_parts;
-    size_t ml_bytes;
-    size_t ws_bytes;
+    int quantum;      // tokens per chunk (unit of work)
+    int part_tokens;  // chunk-aligned tokens per wave slice for the upper-bound batch
+    int num_waves;
+    size_t count_bytes;  // arrival counters, one int per (sequence, KV head)
+    size_t ws_bytes;     // total
 };
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 photon_status plan_decode(const photon_decode_desc *d, Plan *plan)
 {
@@ -102,32 +108,46 @@ photon_status plan_decode(const photon_decode_desc *d, Plan *plan)
     if (group != 1 && group != 2 && group != 4 && group != 8)
         return fail(PHOTON_ERR_UNSUPPORTED, "query heads per KV head %d not built (1, 2, 4, 8 are)",
                     group);
-    if (d->num_seqs > 65535)
-        return fail(PHOTON_ERR_UNSUPPORTED, "num_seqs %d above the grid limit", d->num_seqs);
+    if (d->num_seqs > photon::kMaxDecodeSeqs)
+        return fail(PHOTON_ERR_UNSUPPORTED, "num_seqs %d above %d", d->num_seqs,
+                    photon::kMaxDecodeSeqs);
 
     Plan p{};
     p.group = group;
     p.elem_bytes = elem_bytes_of(d->kv.dtype);
     p.quantum = photon::decode_chunk_tokens(p.elem_bytes, d->kv.head_dim, group);
+    // Units of the largest batch this descriptor allows (every sequence at
+    // max_context_len); the kernel splits the actual units evenly over the
+    // waves, so the slice a wave gets is at most part_tokens.
+    const int64_t chunks = ((int64_t)d->max_context_len + p.quantum - 1) / p.quantum;
+    const int64_t upper = (int64_t)d->num_seqs * d->kv.num_kv_heads * chunks;
+    int64_t waves;
     if (d->partition_tokens > 0) {
         if (d->partition_tokens % p.quantum != 0)
             return fail(PHOTON_ERR_INVALID_ARG, "partition_tokens %d is not a multiple of %d",
                         d->partition_tokens, p.quantum);
-        p.part_tokens = d->partition_tokens;
+        const int64_t per_wave = d->partition_tokens / p.quantum;
+        waves = (upper + per_wave - 1) / per_wave;
     } else {
-        const int64_t pairs = (int64_t)d->num_seqs * d->kv.num_kv_heads;
-        int part = photon::kDecodeWaves * p.quantum;
-        while (part < kMaxAutoPartition &&
-               pairs * ((d->max_context_len + part - 1) / part) > kTargetWorkgroups)
-            part *= 2;
-        p.part_tokens = part;
+        const int64_t unit_bytes = 2LL * p.quantum * d->kv.head_dim * p.elem_bytes;  // K + V
+        int64_t per_cu = kBytesInFlightPerCu / unit_bytes;
+        per_cu = per_cu < kMinWavesPerCu ? kMinWavesPerCu : per_cu;
+        const int64_t auto_waves = kComputeUnits * per_cu;
+        waves = upper < auto_waves ? upper : auto_waves;
     }
-    const int64_t parts = ((int64_t)d->max_context_len + p.part_tokens - 1) / p.part_tokens;
-    p.max_parts = parts < 1 ? 1 : (int)parts;
-    if (p.max_parts > 1) {
-        const size_t rows = (size_t)d->num_seqs * d->num_q_heads * p.max_parts;
-        p.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
-        p.ws_bytes = p.ml_bytes + rows * d->kv.head_dim * sizeof(float);
+    if (waves > kMaxWaves)
+        return fail(PHOTON_ERR_UNSUPPORTED, "%lld wavefronts needed, at most %lld",
+                    (long long)waves, (long long)kMaxWaves);
+    if (waves < 1)
+        waves = 1;
+    waves = (waves + photon::kDecodeWaves - 1) / photon::kDecodeWaves * photon::kDecodeWaves;
+    p.num_waves = (int)waves;
+    const int64_t per_wave = upper > 0 ? (upper + waves - 1) / waves : 1;
+    p.part_tokens = (int)(per_wave * p.quantum);
+    if (d->num_seqs > 0) {
+        const size_t rec = (size_t)photon::decode_record_floats(d->kv.head_dim, group) * sizeof(float);
+        p.count_bytes = align256((size_t)d->num_seqs * d->kv.num_kv_heads * sizeof(int));
+        p.ws_bytes = p.count_bytes + (size_t)waves * 2 * rec;
     }
     *plan = p;
     return PHOTON_OK;
@@ -209,7 +229,7 @@ photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const
     if (workspace_bytes < p.ws_bytes)
         return fail(PHOTON_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
                     p.ws_bytes);
-    if (p.ws_bytes > 0 && (!workspace || !aligned16(workspace)))
+    if (!workspace || !aligned16(workspace))
         return fail(PHOTON_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
 
     photon::DecodeArgs a{};
@@ -219,17 +239,16 @@ photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.out = out;
-    a.ws_ml = p.ws_bytes ? static_cast<float *>(workspace) : nullptr;
-    a.ws_o = p.ws_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ml_bytes)
-                        : nullptr;
+    char *ws = static_cast<char *>(workspace);
+    a.ws_count = reinterpret_cast<int *>(ws);
+    a.ws_rec = reinterpret_cast<float *>(ws + p.count_bytes);
     a.num_seqs = desc->num_seqs;
     a.num_kv_heads = desc->kv.num_kv_heads;
     a.group = p.group;
     a.head_dim = desc->kv.head_dim;
     a.elem_bytes = p.elem_bytes;
     a.max_blocks = desc->max_blocks_per_seq;
-    a.part_tokens = p.part_tokens;
-    a.max_parts = p.max_parts;
+    a.num_waves = p.num_waves;
     a.qscale = (float)((double)scale * 1.4426950408889634);  // log2(e)
     hipError_t err = photon::launch_paged_decode(a, (hipStream_t)stream);
     if (err != hipSuccess)

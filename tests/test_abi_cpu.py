@@ -88,25 +88,28 @@ def test_cache_write_with_no_tokens_launches_nothing():
 
 
 def test_partition_quantum_and_auto_size():
-    # fp32 / d64 / group 4: two 16-token blocks per wave step
+    # fp32 / d64 / group 4: two 16-token blocks per unit of work
     assert pa.lib.photon_paged_attn_partition_quantum(ctypes.byref(dd())) == 32
-    # group 8 with fp32 rows: one block per step keeps the partial scores in registers
+    # group 8 with fp32 rows: one block per unit keeps the partial scores in registers
     assert pa.lib.photon_paged_attn_partition_quantum(ctypes.byref(dd(hq=64))) == 16
     # fp16 / d128 / group 2
     assert pa.lib.photon_paged_attn_partition_quantum(
         ctypes.byref(dd(hq=16, d=128, dtype=pa.F16))) == 32
-    p = pa.lib.photon_paged_attn_partition_tokens(ctypes.byref(dd()))
-    assert p > 0 and p % 32 == 0
+    # auto: 16 seqs x 8 KV heads x 64 units = 8192 units over 1024 waves
+    assert pa.lib.photon_paged_attn_partition_tokens(ctypes.byref(dd())) == 8 * 32
+    # 3 units per wave -> 2731 waves, rounded up to whole workgroups
     assert pa.lib.photon_paged_attn_partition_tokens(ctypes.byref(dd(part=96))) == 96
+    # a small batch gets one wave per unit
+    assert pa.lib.photon_paged_attn_partition_tokens(ctypes.byref(dd(b=1, maxctx=512))) == 32
 
 
 def test_workspace_size_formula():
+    # 3 seqs x 2 KV heads x ceil(640/32) = 120 units; 2 units per wave -> 60 waves
     d = dd(b=3, hq=8, mb=40, maxctx=640, part=64, hkv=2)
-    parts = 10
-    ml = (3 * 8 * parts * 2 * 4 + 255) // 256 * 256
-    assert pa.workspace_bytes(d) == ml + 3 * 8 * parts * 64 * 4
-    # a single partition needs no workspace
-    assert pa.workspace_bytes(dd(b=3, hq=8, mb=40, maxctx=640, part=640, hkv=2)) == 0
+    counters = (3 * 2 * 4 + 255) // 256 * 256
+    record = (2 * 4 + 4 * 64) * 4
+    assert pa.workspace_bytes(d) == counters + 60 * 2 * record
+    assert pa.workspace_bytes(dd(b=0)) == 0
 
 
 @pytest.mark.parametrize("desc,code", [
@@ -118,7 +121,7 @@ def test_workspace_size_formula():
     (dd(part=48), pa.ERR_INVALID_ARG),          # not a multiple of the quantum
     (dd(part=-32), pa.ERR_INVALID_ARG),
     (dd(b=-1), pa.ERR_INVALID_ARG),
-    (dd(b=70000), pa.ERR_UNSUPPORTED),
+    (dd(b=2049), pa.ERR_UNSUPPORTED),
     (dd(bs=32), pa.ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_descriptor(desc, code):

@@ -235,3 +235,25 @@ def test_large_and_negative_scores(pa, scale):
     for part in (0, 64):
         got = gpu_decode(pa, q, kc, vc, tables, ctx, scale, part=part)
         assert_close(got, ref, np.float32, f"scale {scale}")
+
+
+def test_workspace_reused_across_calls_stays_zeroed(pa):
+    # Arrival counters live at the start of the workspace; every call must
+    # leave them at zero so one workspace serves calls of any shape.
+    rng = np.random.default_rng(27)
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 9, 32, 8, 64, max_ctx=900)
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    args = [dev(q), dev(kc), dev(vc), dev(tables), dev(ctx)]
+    sizes = {}
+    for part in (32, 64, 128, 256):
+        desc = pa.decode_desc(args[0], args[1], args[3], int(ctx.max()), part)
+        sizes[part] = pa.workspace_bytes(desc)
+    ws = pa.new_workspace(max(sizes.values()), "cuda:0")
+    for rep in range(2):
+        for part in (32, 64, 128, 256):
+            out = pa.paged_attn_decode(*args, 0.125, max_context_len=int(ctx.max()), workspace=ws,
+                                       partition_tokens=part)
+            torch.cuda.synchronize()
+            assert_close(host(out), ref, np.float32, f"partition {part} rep {rep}")
+            counters = host(ws[: 9 * 8 * 4].view(torch.int32))
+            assert (counters == 0).all(), f"counters left at {counters[counters != 0]}"
