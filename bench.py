@@ -1,9 +1,9 @@
 """Benchmark of the batched paged-attention decode step on one MI355X.
 
-One step is the whole hot path over one synthetic batch: for each of the
-workload's layers, the slot-mapped cache write of the batch's new tokens and
-the paged decode over the block tables (one kernel; split contexts merge
-inside it).  Inputs are generated once, copied to HBM, and stay
+One step is the whole hot path over one synthetic batch: the slot-mapped
+cache write of the batch's new tokens into every layer's pool, then the paged
+decode of every layer over the block tables (one kernel per call; split
+contexts merge inside it).  Each layer's decode follows its own write.  Inputs are generated once, copied to HBM, and stay
 resident; every layer owns its own K/V pool, so a 16-layer step touches about
 1.1 GB and the 256 MiB Infinity Cache cannot serve repeated reads.
 
@@ -11,8 +11,9 @@ Printed: one JSON line.  ``value`` is whole-step throughput in algorithmic
 GB/s (bytes the method must move: valid K/V rows, q, out, table entries and
 lengths for the decode; k/v rows and slots for the write) per measured step
 time.  ``roofline`` describes the decode kernel (one launch per decode call;
-split contexts merge inside it), timed with HIP events recorded on the
-launch stream around every decode call inside the timed region.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
+split contexts merge inside it): its average launch time is the event-timed
+run of one step's decode launches (events recorded on the launch stream)
+divided by the number of launches.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
 the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama1b_b16]
@@ -20,8 +21,10 @@ the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -31,6 +34,32 @@ import numpy as np
 import decode_inputs as di
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["paged_attention_decode_photon_amd/csrc/paged_decode.hip",
+                  "paged_attention_decode_photon_amd/csrc/lane_ops.h",
+                  "paged_attention_decode_photon_amd/csrc/launch.h"]
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.]+)", text)
+    if not sha or not val or sha.group(1) != kernel_source_sha256():
+        return None
+    return float(val.group(1))
 
 
 def decode_bytes(cfg: di.DecodeConfig, ctx: np.ndarray) -> int:
@@ -58,6 +87,11 @@ def parse_args(argv=None):
     ap.add_argument("--partition-tokens", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before warm-up, copy a buffer of this many MiB once (a plain "
+                         "device copy of known size, used to scale HBM byte counters)")
+    ap.add_argument("--copy-bw-mib", type=int, default=1024,
+                    help="size of the device-to-device copy timed for context (0 disables)")
     ap.add_argument("--min-step-gib", type=float, default=1.0,
                     help="the workload's layers are replicated (fresh pools) until one step "
                          "reads at least this much distinct K/V, so no layer is served from "
@@ -144,32 +178,70 @@ def main(argv=None) -> int:
                                               lens.data_ptr(), scale, descref, L["out"].data_ptr(),
                                               workspace.data_ptr(), ws_bytes, sptr))
 
-    n_events = len(layers) * args.steps
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    copy_gbps = None
+    if args.copy_bw_mib > 0:
+        # achievable read+write rate of a plain device copy, for context
+        n = args.copy_bw_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * n * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+        del src, dst
+
+    def event():
+        return torch.cuda.Event(enable_timing=True)
 
     for _ in range(args.warmup):
         for L in layers:
             write(L)
+        for L in layers:
             decode(L)
     torch.cuda.synchronize()
 
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region.  A step writes every layer's new tokens, then decodes
+    # every layer (each decode follows its own layer's write); one event pair
+    # brackets each step's run of decode launches, on the launch stream.
+    burst = [(event(), event()) for _ in range(args.steps)]
+    start, stop = event(), event()
     start.record(stream)
-    i = 0
-    for _ in range(args.steps):
+    for i in range(args.steps):
         for L in layers:
             write(L)
-            ev_a[i].record(stream)
+        burst[i][0].record(stream)
+        for L in layers:
             decode(L)
-            ev_b[i].record(stream)
-            i += 1
+        burst[i][1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(stop) / args.steps
-    call_us = [a.elapsed_time(b) * 1e3 for a, b in zip(ev_a, ev_b)]
-    call_mean = statistics.fmean(call_us)
-    call_med = statistics.median(call_us)
+    burst_us = [a.elapsed_time(b) * 1e3 / len(layers) for a, b in burst]
+    call_mean = statistics.fmean(burst_us)
+    call_med = statistics.median(burst_us)
+
+    # Secondary: events around every single decode call (adds the event
+    # packets' own overhead to each launch).
+    single = [(event(), event()) for _ in layers]
+    for (a, b), L in zip(single, layers):
+        a.record(stream)
+        decode(L)
+        b.record(stream)
+    torch.cuda.synchronize()
+    single_us = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in single)
 
     per_decode = decode_bytes(cfg, lay.context_lens)
     n_written = int((lay.slot_mapping >= 0).sum())
@@ -210,15 +282,18 @@ def main(argv=None) -> int:
         "tokens_per_s_per_layer": round(tok_per_layer, 1),
         "decode_call_us_mean": round(call_mean, 3),
         "decode_call_us_median": round(call_med, 3),
+        "decode_call_us_single_event_pair": round(single_us, 3),
         "decode_gbps_event_timed": round(achieved, 2),
+        "copy_gbps_read_plus_write": round(copy_gbps, 1) if copy_gbps else None,
+        "kernel_source_sha256": kernel_source_sha256(),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
-            "kernel": "paged_decode_partition (one launch per photon_paged_attn_decode call)",
+            "traffic": measured_traffic(cfg.name),
+            "kernel": "paged_decode_kernel (one launch per photon_paged_attn_decode call)",
             "bytes_per_launch": per_decode,
         },
     }
