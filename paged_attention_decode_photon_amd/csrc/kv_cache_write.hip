@@ -18,24 +18,32 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ v, const int32_t *__restrict__ slots,
-    int64_t total_chunks, u32x4 *__restrict__ k_cache, u32x4 *__restrict__ v_cache,
-    int num_kv_heads, int block_size, int chunks_per_row)
+    u32x4 *__restrict__ k_cache, u32x4 *__restrict__ v_cache, int num_kv_heads, int block_size,
+    int chunks_per_row)
 {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total_chunks)
+    // Block x = token (so its slot is a wave-uniform scalar load); y and the
+    // thread index cover that token's (head, 16-byte chunk) pairs.
+    const int64_t token = blockIdx.x;
+    const int i = blockIdx.y * blockDim.x + threadIdx.x;
+    const int per_token = num_kv_heads * chunks_per_row;
+    if (i >= per_token)
         return;
-    const int chunk = (int)(idx % chunks_per_row);
-    const int64_t row = idx / chunks_per_row;  // = token * num_kv_heads + head
-    const int h = (int)(row % num_kv_heads);
-    const int64_t token = row / num_kv_heads;
+    const int64_t src = token * per_token + i;
+    const u32x4 kr = k[src];
+    const u32x4 vr = v[src];
     const int32_t slot = slots[token];
+    // Keep the row loads in flight together with the slot load rather than
+    // letting the compiler sink them below the slot test.
+    asm volatile("" ::"v"(kr), "v"(vr), "s"(slot));
     if (slot < 0)
         return;
+    const int h = i / chunks_per_row;
+    const int chunk = i - h * chunks_per_row;
     const int64_t blk = slot / block_size;
-    const int64_t off = slot % block_size;
+    const int64_t off = slot - blk * block_size;
     const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * chunks_per_row + chunk;
-    k_cache[dst] = k[idx];
-    v_cache[dst] = v[idx];
+    k_cache[dst] = kr;
+    v_cache[dst] = vr;
 }
 
 }  // namespace
@@ -45,12 +53,12 @@ hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *sl
                                  int block_size, int row_bytes, hipStream_t stream)
 {
     const int chunks_per_row = row_bytes / 16;
-    const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks_per_row;
     const int threads = 256;
-    const int64_t blocks = (total + threads - 1) / threads;
-    hipLaunchKernelGGL(kv_cache_write_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       (const u32x4 *)k, (const u32x4 *)v, slots, total, (u32x4 *)k_cache,
-                       (u32x4 *)v_cache, num_kv_heads, block_size, chunks_per_row);
+    const int per_token = num_kv_heads * chunks_per_row;
+    const dim3 grid((unsigned)num_tokens, (unsigned)((per_token + threads - 1) / threads));
+    hipLaunchKernelGGL(kv_cache_write_kernel, grid, dim3(threads), 0, stream, (const u32x4 *)k,
+                       (const u32x4 *)v, slots, (u32x4 *)k_cache, (u32x4 *)v_cache, num_kv_heads,
+                       block_size, chunks_per_row);
     return hipGetLastError();
 }
 

@@ -257,3 +257,39 @@ def test_workspace_reused_across_calls_stays_zeroed(pa):
             assert_close(host(out), ref, np.float32, f"partition {part} rep {rep}")
             counters = host(ws[: 9 * 8 * 4].view(torch.int32))
             assert (counters == 0).all(), f"counters left at {counters[counters != 0]}"
+
+
+def test_hip_graph_replays_match_eager(pa):
+    # Write + decode captured in a HIP graph and replayed several times, with
+    # eager work in between; every replay must equal the eager result.
+    cfg = di.CONFIGS["cb_b64"]
+    lay = di.make_layout(cfg)
+    t = di.make_layer(cfg, lay)
+    q, kn, vn = dev(t.q), dev(t.k_new), dev(t.v_new)
+    tables, lens, slots = dev(lay.block_tables), dev(lay.context_lens), dev(lay.slot_mapping)
+    kc0, vc0 = dev(t.k_cache), dev(t.v_cache)
+    desc = pa.decode_desc(q, kc0, tables, lay.max_context_len)
+    ws = pa.new_workspace(pa.workspace_bytes(desc), "cuda:0")
+    kc, vc = kc0.clone(), vc0.clone()
+    eager = torch.empty_like(q)
+    pa.kv_cache_write(kn, vn, slots, kc, vc)
+    pa.paged_attn_decode(q, kc, vc, tables, lens, cfg.scale, max_context_len=lay.max_context_len,
+                         out=eager, workspace=ws)
+    torch.cuda.synchronize()
+    kc, vc = kc0.clone(), vc0.clone()
+    out = torch.zeros_like(q)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pa.kv_cache_write(kn, vn, slots, kc, vc)
+        pa.paged_attn_decode(q, kc, vc, tables, lens, cfg.scale,
+                             max_context_len=lay.max_context_len, out=out, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert host(out).tobytes() == host(eager).tobytes(), f"replay {rep} differs"
+        # eager work between replays, on the same workspace
+        other = pa.paged_attn_decode(q, kc, vc, tables, lens, cfg.scale,
+                                     max_context_len=lay.max_context_len, workspace=ws)
+        torch.cuda.synchronize()
+        assert host(other).tobytes() == host(eager).tobytes()
