@@ -149,7 +149,7 @@ def main(argv=None) -> int:
     copies = int(min(512 // n_layers, max(1, -(-int(args.min_step_gib * 2**30) // pool_bytes))))
 
     def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return di.to_torch(a).to(device)
 
     tables, lens, slots = up(lay.block_tables), up(lay.context_lens), up(lay.slot_mapping)
     layers = []

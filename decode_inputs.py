@@ -21,7 +21,7 @@ Recipe (all draws from ``numpy.random.default_rng``):
   permutation, so the pool is shared and shuffled;
 * per-layer tensors come from ``default_rng([seed, layer])`` in the order
   q, K pool, V pool, new k, new v, each ``standard_normal`` in float32 and
-  then cast to the storage dtype;
+  then rounded to nearest (ties to even) in the storage dtype;
 * the decode-step slot of sequence b is the logical position ``ctx_b - 1``
   (the new token is written first and then attended to).
 """
@@ -35,7 +35,73 @@ import numpy as np
 BLOCK_SIZE = 16
 PAD_TABLE_ENTRY = -1
 
-_NP_DTYPE = {"f32": np.float32, "f16": np.float16}
+# numpy has no bfloat16: bf16 arrays are held as this one-field record of
+# the 16 storage bits, so that they cannot be mistaken for integers.  Never
+# ``astype`` into it (numpy would cast values to integers field-wise); use
+# ``to_storage``.
+BF16 = np.dtype([("bf16", "<u2")])
+
+_NP_DTYPE = {"f32": np.dtype(np.float32), "f16": np.dtype(np.float16), "bf16": BF16}
+# Quiet-NaN bit patterns, used to poison pool slots no sequence may read.
+_NAN_BITS = {np.dtype(np.float32): (np.uint32, 0x7FC00000),
+             np.dtype(np.float16): (np.uint16, 0x7E00),
+             BF16: (np.uint16, 0x7FC0)}
+
+
+def to_storage(x: np.ndarray, dtype) -> np.ndarray:
+    """float32 values rounded to nearest-even in storage dtype ``dtype``.
+
+    For bfloat16 (the upper half of a binary32) the rounding is done on the
+    bits: add 0x7FFF plus the lowest kept bit, then drop the low 16 bits;
+    NaN stays a quiet NaN of the same sign.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    dtype = np.dtype(dtype)
+    if dtype != BF16:
+        return x.astype(dtype)
+    bits = x.view(np.uint32).astype(np.uint64)
+    rounded = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    rounded[nan] = (bits[nan] >> 16).astype(np.uint16) | 0x7FC0
+    return rounded.view(BF16)
+
+
+def cast(x: np.ndarray, dtype) -> np.ndarray:
+    """``x.astype(dtype)`` for float32/float16; ``to_storage`` (via float32) for ``BF16``."""
+    dtype = np.dtype(dtype)
+    if dtype == BF16:
+        return to_storage(np.asarray(x, dtype=np.float32), BF16)
+    return np.asarray(x).astype(dtype)
+
+
+def as_float64(a: np.ndarray) -> np.ndarray:
+    """Exact float64 values of a storage array (torch widens bfloat16)."""
+    if a.dtype == BF16:
+        return to_torch(a).double().numpy()
+    return np.asarray(a).astype(np.float64)
+
+
+def storage_bits(a: np.ndarray) -> np.ndarray:
+    """Unsigned-integer view of a storage array's bits (same shape)."""
+    return a.view(_NAN_BITS[a.dtype][0])
+
+
+def to_torch(a: np.ndarray):
+    """CPU torch tensor sharing ``a``'s bits (bfloat16 for ``BF16`` arrays)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == BF16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(a)
+
+
+def from_torch(t) -> np.ndarray:
+    """numpy copy of a torch tensor's bits (``BF16`` for bfloat16)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(BF16)
+    return t.numpy()
 
 
 @dataclasses.dataclass(frozen=True)
@@ -48,7 +114,7 @@ class DecodeConfig:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    dtype: str  # "f32" or "f16": storage type of q, K/V pool and output
+    dtype: str  # "f32", "f16" or "bf16": storage type of q, K/V pool and output
     ctx_kind: str  # "fixed", "uniform" or "loguniform"
     ctx_lo: int
     ctx_hi: int
@@ -91,6 +157,9 @@ CONFIGS: dict[str, DecodeConfig] = {
     # Qwen3-0.6B-shaped long context, fp16 KV, head_dim 128.
     "qwen3_long": DecodeConfig("qwen3_long", 4, 8, 16, 8, 128, "f16",
                                "fixed", 32768, 32768),
+    # The batch-16 Llama step with bfloat16 KV (same seed, contexts, tables).
+    "llama1b_b16_bf16": DecodeConfig("llama1b_b16_bf16", 2, 16, 32, 8, 64, "bf16",
+                                     "uniform", 64, 2048, layers=16),
 }
 
 
@@ -176,7 +245,7 @@ def make_layer(cfg: DecodeConfig, layout: BatchLayout, layer: int = 0,
     t = b if num_new_tokens is None else num_new_tokens
 
     def draw(shape):
-        return rng.standard_normal(shape, dtype=np.float32).astype(dt, copy=False)
+        return to_storage(rng.standard_normal(shape, dtype=np.float32), dt)
 
     q = draw((b, hq, d))
     k_cache = draw((layout.num_blocks, hkv, bs, d))
@@ -195,10 +264,6 @@ def random_injective_slots(num_blocks: int, block_size: int, n: int,
     return slots
 
 
-def nan_value(dtype) -> np.generic:
-    return np.array(np.nan, dtype=dtype)[()]
-
-
 def poison_unused(cfg: DecodeConfig, layout: BatchLayout, pool: np.ndarray) -> np.ndarray:
     """Copy of ``pool`` with NaN in every slot no sequence may read.
 
@@ -206,14 +271,15 @@ def poison_unused(cfg: DecodeConfig, layout: BatchLayout, pool: np.ndarray) -> n
     last block at or past its context length.
     """
     out = pool.copy()
+    bits = storage_bits(out)
     bs = cfg.block_size
     used = np.zeros(layout.num_blocks, dtype=bool)
-    nan = nan_value(pool.dtype)
+    nan = _NAN_BITS[pool.dtype][1]
     for b, c in enumerate(layout.context_lens):
         n = int(blocks_needed(np.array([c]), bs)[0])
         used[layout.block_tables[b, :n]] = True
         if c % bs:
             last = layout.block_tables[b, n - 1]
-            out[last, :, c % bs:, :] = nan
-    out[~used] = nan
+            bits[last, :, c % bs:, :] = nan
+    bits[~used] = nan
     return out

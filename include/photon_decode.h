@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PHOTON_ABI_VERSION 1
+#define PHOTON_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define PHOTON_API __attribute__((visibility("default")))
@@ -58,12 +58,24 @@ typedef enum photon_status {
     PHOTON_ERR_HIP = 4          /* the HIP runtime refused a launch */
 } photon_status;
 
-/* Storage type of q, the K/V pools, new K/V rows and the output.
- * Scores, softmax and accumulation are always fp32. */
+/* Storage type of q, the K/V pools, new K/V rows and (unless
+ * PHOTON_DECODE_OUT_F32 is set) the output.  Scores, softmax and
+ * accumulation are always fp32.  PHOTON_BF16 is bfloat16 (the upper 16 bits
+ * of a binary32), the half-precision type the README's roadmap names next to
+ * FP16. */
 typedef enum photon_dtype {
     PHOTON_F32 = 0,
-    PHOTON_F16 = 1
+    PHOTON_F16 = 1,
+    PHOTON_BF16 = 2
 } photon_dtype;
+
+/* photon_decode_desc.flags */
+enum {
+    /* Write the decode output as fp32 whatever kv.dtype is (a no-op for
+     * PHOTON_F32): the output row is then the fp32 accumulation, normalised,
+     * without a final rounding to 16 bits. */
+    PHOTON_DECODE_OUT_F32 = 1
+};
 
 /* Shape of one KV block pool (K and V pools have the same shape). */
 typedef struct photon_kv_desc {
@@ -92,6 +104,8 @@ typedef struct photon_decode_desc {
                                    actual batch is always split evenly over
                                    the wavefronts this implies                   */
     photon_kv_desc kv;
+    int32_t flags;              /* PHOTON_DECODE_* bits, 0 = none; other bits
+                                   are PHOTON_ERR_INVALID_ARG                    */
 } photon_decode_desc;
 
 /*
@@ -166,7 +180,8 @@ PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_d
  *   k_cache, v_cache  pools (read only), 16-byte aligned
  *   block_tables  [num_seqs, max_blocks_per_seq] int32, entries < kv.num_blocks
  *   context_lens  [num_seqs] int32, 0 <= ctx <= max_context_len
- *   out           [num_seqs, num_q_heads, head_dim]        kv.dtype, 16-byte aligned
+ *   out           [num_seqs, num_q_heads, head_dim]        kv.dtype (fp32 with
+ *                 PHOTON_DECODE_OUT_F32), 16-byte aligned
  *   workspace     device scratch of workspace_bytes >= the size the workspace
  *                 query returns, 16-byte aligned, zero-filled before its first
  *                 use

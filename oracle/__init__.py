@@ -11,8 +11,8 @@ Parity pins (all in ``tests/test_oracle_*.py``): hand-derived golden cases,
 dense attention through ``torch.nn.functional.scaled_dot_product_attention``,
 closed forms (one token, constant V, zero query, dominant key), invariance
 under a permutation of physical blocks, GQA equal to MHA with repeated KV
-heads, softmax rows summing to one, the binary16 decoder over all 65536 bit
-patterns, brute-force cache writes and the precondition error codes.
+heads, softmax rows summing to one, the binary16 and bfloat16 decoders over
+all 65536 bit patterns each, brute-force cache writes and the precondition error codes.
 """
 from __future__ import annotations
 
@@ -34,7 +34,11 @@ ERR_BLOCK_RANGE = 4
 ERR_CTX = 5
 ERR_HEADS = 6
 
-_DTYPE_CODE = {np.dtype(np.float32): 0, np.dtype(np.float16): 1}
+# Storage types: float32, float16, and bfloat16 held as a one-field record of
+# its 16 bits (the input module's ``BF16``; any uint16 record dtype is read as
+# bfloat16 bits).
+_BF16 = np.dtype([("bf16", "<u2")])
+_DTYPE_CODE = {np.dtype(np.float32): 0, np.dtype(np.float16): 1, _BF16: 2}
 
 
 class OracleError(RuntimeError):
@@ -60,6 +64,8 @@ def _configure(lib):
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = ctypes.c_double
+    lib.oracle_bfloat16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bfloat16_to_double.restype = ctypes.c_double
     lib.oracle_kv_cache_write.argtypes = [vp, vp, vp, i64, vp, vp, i64, i64, i64, i64, i64]
     lib.oracle_kv_cache_write.restype = ctypes.c_int
     lib.oracle_paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
@@ -106,6 +112,10 @@ def _ptr(a: np.ndarray | None):
 
 def half_to_double(bits: int) -> float:
     return _load().oracle_half_to_double(int(bits) & 0xFFFF)
+
+
+def bfloat16_to_double(bits: int) -> float:
+    return _load().oracle_bfloat16_to_double(int(bits) & 0xFFFF)
 
 
 def max_threads() -> int:

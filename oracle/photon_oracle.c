@@ -40,7 +40,7 @@ enum {
     ORACLE_ERR_HEADS = 6        /* num_q_heads not a multiple of num_kv_heads */
 };
 
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
 
 /* IEEE 754 binary16 -> double, from the format's definition: 1 sign bit,
  * 5 exponent bits (bias 15), 10 fraction bits; exponent 0 encodes zero and
@@ -60,11 +60,31 @@ double oracle_half_to_double(uint16_t bits)
     return sign ? -mag : mag;
 }
 
+/* bfloat16 -> double, from the format's definition: 1 sign bit, 8 exponent
+ * bits (bias 127, as binary32), 7 fraction bits; exponent 0 encodes zero and
+ * subnormals (fraction * 2^-133), exponent 255 encodes inf / NaN. */
+double oracle_bfloat16_to_double(uint16_t bits)
+{
+    const int sign = bits >> 15;
+    const int expo = (bits >> 7) & 0xff;
+    const int frac = bits & 0x7f;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -133);
+    else if (expo == 255)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(frac | 0x80), expo - 134);
+    return sign ? -mag : mag;
+}
+
 static double widen(const void *base, int64_t idx, int dtype)
 {
     if (dtype == ORACLE_F32)
         return (double)((const float *)base)[idx];
-    return oracle_half_to_double(((const uint16_t *)base)[idx]);
+    if (dtype == ORACLE_F16)
+        return oracle_half_to_double(((const uint16_t *)base)[idx]);
+    return oracle_bfloat16_to_double(((const uint16_t *)base)[idx]);
 }
 
 /* Cache write: for each token i with slot >= 0, copy the raw bytes of
@@ -138,7 +158,7 @@ int oracle_paged_attn_decode(const void *q, const void *k_cache, const void *v_c
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks <= 0 || max_blocks <= 0 ||
-        (dtype != ORACLE_F32 && dtype != ORACLE_F16))
+        (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
         return ORACLE_ERR_ARG;
     if (num_q_heads % num_kv_heads != 0)
         return ORACLE_ERR_HEADS;

@@ -29,6 +29,9 @@ ERR_HIP = 4
 
 F32 = 0
 F16 = 1
+BF16 = 2
+
+DECODE_OUT_F32 = 1  # photon_decode_desc.flags: fp32 output for 16-bit storage
 
 BLOCK_SIZE = 16
 
@@ -52,7 +55,7 @@ class KvDesc(ctypes.Structure):
 class DecodeDesc(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
-                ("partition_tokens", ctypes.c_int32), ("kv", KvDesc)]
+                ("partition_tokens", ctypes.c_int32), ("kv", KvDesc), ("flags", ctypes.c_int32)]
 
 
 def _hip_runtimes_mapped() -> set[str]:
@@ -112,6 +115,8 @@ def _dtype_code(t) -> int:
         return F32
     if t.dtype == torch.float16:
         return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
     raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", f"dtype {t.dtype} not supported")
 
 
@@ -131,10 +136,10 @@ def kv_desc(k_cache) -> KvDesc:
 
 
 def decode_desc(q, k_cache, block_tables, max_context_len: int,
-                partition_tokens: int = 0) -> DecodeDesc:
+                partition_tokens: int = 0, flags: int = 0) -> DecodeDesc:
     b, hq, _ = q.shape
     return DecodeDesc(b, hq, block_tables.shape[1], int(max_context_len), int(partition_tokens),
-                      kv_desc(k_cache))
+                      kv_desc(k_cache), int(flags))
 
 
 def kv_cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
@@ -184,7 +189,7 @@ def new_workspace(nbytes: int, device):
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
                       max_context_len: int | None = None, out=None, workspace=None,
-                      partition_tokens: int = 0):
+                      partition_tokens: int = 0, out_dtype=None):
     """GQA paged decode: out[b, h] = softmax(scale q K^T) V over context_lens[b] tokens.
 
     q, out: [B, Hq, D]; pools: [NB, Hkv, 16, D]; block_tables: [B, max_blocks]
@@ -192,6 +197,8 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
     context length (if None it is read back from the device, which
     synchronises).  ``workspace`` (uint8 device tensor from
     :func:`new_workspace`) is allocated through torch when not given and needed.
+    ``out`` (or ``out_dtype`` when ``out`` is None) is q's dtype or float32;
+    float32 with 16-bit storage selects the fp32-output kernels.
     """
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
@@ -207,14 +214,22 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
     if max_context_len is None:
         max_context_len = int(context_lens.max().item()) if context_lens.numel() else 0
-    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens)
+    if out is not None:
+        out_dtype = out.dtype
+    elif out_dtype is None:
+        out_dtype = q.dtype
+    if out_dtype not in (q.dtype, torch.float32):
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          f"output dtype {out_dtype} is neither {q.dtype} nor float32")
+    flags = DECODE_OUT_F32 if out_dtype == torch.float32 and q.dtype != torch.float32 else 0
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens, flags)
     ws_need = workspace_bytes(desc)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     else:
         _contig("out", out)
-        if out.shape != q.shape or out.dtype != q.dtype:
-            raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape or dtype")
+        if out.shape != q.shape:
+            raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape")
     if ws_need and workspace is None:
         workspace = new_workspace(ws_need, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None

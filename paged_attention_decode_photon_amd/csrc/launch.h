@@ -12,15 +12,17 @@ namespace photon {
 #ifndef PHOTON_DECODE_WAVES
 #define PHOTON_DECODE_WAVES 4    // wavefronts per decode workgroup
 #endif
-#ifndef PHOTON_DECODE_PREFETCH
-#define PHOTON_DECODE_PREFETCH 0 // 1: load the next chunk before consuming the current one
-#endif
 #ifndef PHOTON_KV_LOAD_AUX
 #define PHOTON_KV_LOAD_AUX 0     // cache-policy bits of the K/V buffer loads
 #endif
 #ifndef PHOTON_DECODE_CHUNK_BLOCKS
 #define PHOTON_DECODE_CHUNK_BLOCKS 0  // KV blocks per unit of work; 0: shape rule below
 #endif
+
+// Storage types (the values of photon_dtype).
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeF16 = 1;
+constexpr int kDtypeBF16 = 2;
 
 constexpr int kBlockTokens = 16;     // tokens per KV block the decode kernels are built for
 constexpr int kDecodeWaves = PHOTON_DECODE_WAVES;
@@ -66,6 +68,8 @@ struct DecodeArgs {
     int group;
     int head_dim;
     int elem_bytes;
+    int dtype;      // kDtype* of q and the pools
+    int out_f32;    // 1: out is fp32 whatever the storage type
     int max_blocks;
     int num_waves;  // wavefronts launched; a multiple of kDecodeWaves
     float qscale;   // scale * log2(e)

@@ -71,6 +71,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
 // Fourth descriptor word of a raw (unswizzled, stride 0) buffer on gfx9-family.
 constexpr int kRawBufferWord3 = 0x00020000;
@@ -128,6 +129,51 @@ struct Elem<_Float16> {
     }
     __device__ static _Float16 from_float(float x) { return (_Float16)x; }
 };
+
+// bfloat16 is the upper half of a binary32, so widening is a shift; narrowing
+// rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <>
+struct Elem<__bf16> {
+    __device__ static void unpack(const u32x4 &v, float (&f)[8])
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t word = v[i];
+            f[2 * i] = __uint_as_float(word << 16);
+            f[2 * i + 1] = __uint_as_float(word & 0xffff0000u);
+        }
+    }
+    __device__ static u32x4 pack(const float (&f)[8])
+    {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf162_t h;
+            h[0] = (__bf16)f[2 * i];
+            h[1] = (__bf16)f[2 * i + 1];
+            const uint32_t word = __builtin_bit_cast(uint32_t, h);
+            v[i] = word;
+        }
+        return v;
+    }
+    __device__ static __bf16 from_float(float x) { return (__bf16)x; }
+};
+
+// Store E consecutive outputs of type O (E * sizeof(O) is 16 or 32 bytes).
+template <typename O, int E>
+__device__ __forceinline__ void store_out(O *dst, const float (&v)[E])
+{
+    if constexpr (sizeof(O) == 4) {
+#pragma unroll
+        for (int k = 0; k < E / 4; ++k)
+            *reinterpret_cast<u32x4 *>(dst + 4 * k) =
+                u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                      __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
+    } else {
+        static_assert(E * sizeof(O) == 16, "one 16-byte store");
+        *reinterpret_cast<u32x4 *>(dst) = Elem<O>::pack(v);
+    }
+}
 
 template <typename T, int D, int G>
 struct Shape {
@@ -220,7 +266,7 @@ __device__ __forceinline__ int slice_of(int u, int total, int nw)
     return (int)((((long long)u + 1) * nw - 1) / total);
 }
 
-template <typename T, int D, int G>
+template <typename T, typename O, int D, int G>
 struct WaveDecoder {
     using S = Shape<T, D, G>;
     static constexpr int E = S::E, L = S::L, RPI = S::RPI, NIB = S::NIB, CT = S::CT;
@@ -423,30 +469,16 @@ struct WaveDecoder {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // Chunks [ch0, ch1) of the current segment.
+    // Chunks [ch0, ch1) of the current segment, one at a time.  (Loading the
+    // next chunk before consuming the current one measured slower: the extra
+    // registers cost occupancy and the loads in flight per CU do not grow.)
     __device__ void run_chunks(int ch0, int ch1)
     {
-        if constexpr (PHOTON_DECODE_PREFETCH) {
-            // Two chunks per step, both loaded before the first is consumed.
-            // The code inside a step is straight-line, so the wait before
-            // each consume covers only that chunk's loads.
-            for (int ch = ch0; ch < ch1; ch += 2) {
-                const bool two = ch + 1 < ch1;
-                cover_blocks(ch * S::U, (ch + 2) * S::U - 1);
-                u32x4 ka[NU], va[NU], kb[NU], vb[NU];
-                load_chunk(ch, ka, va);
-                load_chunk(ch + 1, kb, vb, two);
-                consume_chunk(ch, ka, va);
-                if (two)
-                    consume_chunk(ch + 1, kb, vb);
-            }
-        } else {
-            for (int ch = ch0; ch < ch1; ++ch) {
-                cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
-                u32x4 kd[NU], vd[NU];
-                load_chunk(ch, kd, vd);
-                consume_chunk(ch, kd, vd);
-            }
+        for (int ch = ch0; ch < ch1; ++ch) {
+            cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
+            u32x4 kd[NU], vd[NU];
+            load_chunk(ch, kd, vd);
+            consume_chunk(ch, kd, vd);
         }
     }
 
@@ -466,14 +498,14 @@ struct WaveDecoder {
                 o_acc[h][e] = allreduce_bits<S::LOG2L, 6, OpSum>(o_acc[h][e]);
     }
 
-    __device__ T *out_rows() const
+    __device__ O *out_rows() const
     {
-        return (T *)a.out + ((size_t)b * a.num_kv_heads * G + (size_t)g * G) * D;
+        return (O *)a.out + ((size_t)b * a.num_kv_heads * G + (size_t)g * G) * D;
     }
 
     __device__ void write_output() const
     {
-        T *dst = out_rows();
+        O *dst = out_rows();
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float inv = 1.0f / read_lane(l_run, h);
@@ -482,7 +514,7 @@ struct WaveDecoder {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     v[e] = o_acc[h][e] * inv;
-                *reinterpret_cast<u32x4 *>(dst + (size_t)h * D + c * E) = Elem<T>::pack(v);
+                store_out<O, E>(dst + (size_t)h * D + c * E, v);
             }
         }
     }
@@ -522,7 +554,7 @@ struct WaveDecoder {
         const int s_first = slice_of(su0, total, nw);
         const int s_last = slice_of(su1 - 1, total, nw);
         const int first_role = slice_start(s_first, total, nw) == su0 ? 0 : 1;
-        T *dst = out_rows();
+        O *dst = out_rows();
         compiler_memory_barrier();
         for (int v = lane; v < G * D / 4; v += 64) {
             const int i = 4 * v;  // first of this lane's four outputs
@@ -568,7 +600,7 @@ struct WaveDecoder {
             const float inv = 1.0f / lsum;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                dst[i + e] = Elem<T>::from_float(o[e] * inv);
+                dst[i + e] = Elem<O>::from_float(o[e] * inv);
         }
     }
 };
@@ -594,7 +626,7 @@ __device__ int block_inclusive_scan(int v, int *wave_totals)
     return v + before;
 }
 
-template <typename T, int D, int G>
+template <typename T, typename O, int D, int G>
 __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelArgs a)
 {
     using S = Shape<T, D, G>;
@@ -645,9 +677,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     // Sequences with an empty context have no units; their rows are zero.
     for (int bb = s; bb < B; bb += a.num_waves) {
         if (__builtin_amdgcn_readfirstlane(ctx_lds[bb]) == 0) {
-            T *row = (T *)a.out + (size_t)bb * hkv * G * D;
+            O *row = (O *)a.out + (size_t)bb * hkv * G * D;
             for (int i = lane; i < hkv * G * D; i += 64)
-                row[i] = Elem<T>::from_float(0.0f);
+                row[i] = Elem<O>::from_float(0.0f);
         }
     }
     // Slices over min(waves, units) wavefronts are never empty, so every
@@ -658,7 +690,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     const int u_begin = slice_start(s, total, nw);
     const int u_end = slice_start(s + 1, total, nw);
 
-    WaveDecoder<T, D, G> w(a, p_lds[wave]);
+    WaveDecoder<T, O, D, G> w(a, p_lds[wave]);
 
     // First sequence whose units reach past u_begin.
     int lo = 0, hi = B - 1;
@@ -713,7 +745,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     }
 }
 
-template <typename T, int D, int G>
+template <typename T, typename O, int D, int G>
 hipError_t launch_typed(const DecodeArgs &d, hipStream_t stream)
 {
     KernelArgs a;
@@ -730,42 +762,50 @@ hipError_t launch_typed(const DecodeArgs &d, hipStream_t stream)
     a.max_blocks = d.max_blocks;
     a.num_waves = d.num_waves;
     a.qscale = d.qscale;
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, G>), dim3(d.num_waves / kDecodeWaves),
+    hipLaunchKernelGGL((paged_decode_kernel<T, O, D, G>), dim3(d.num_waves / kDecodeWaves),
                        dim3(kDecodeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename O, int D>
 hipError_t launch_group(const DecodeArgs &a, hipStream_t stream)
 {
     switch (a.group) {
-    case 1: return launch_typed<T, D, 1>(a, stream);
-    case 2: return launch_typed<T, D, 2>(a, stream);
-    case 4: return launch_typed<T, D, 4>(a, stream);
-    case 8: return launch_typed<T, D, 8>(a, stream);
+    case 1: return launch_typed<T, O, D, 1>(a, stream);
+    case 2: return launch_typed<T, O, D, 2>(a, stream);
+    case 4: return launch_typed<T, O, D, 4>(a, stream);
+    case 8: return launch_typed<T, O, D, 8>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T>
+template <typename T, typename O>
 hipError_t launch_dim(const DecodeArgs &a, hipStream_t stream)
 {
     switch (a.head_dim) {
-    case 64: return launch_group<T, 64>(a, stream);
-    case 128: return launch_group<T, 128>(a, stream);
+    case 64: return launch_group<T, O, 64>(a, stream);
+    case 128: return launch_group<T, O, 128>(a, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+// 16-bit storage with the output in its own type or in fp32.
+template <typename T>
+hipError_t launch_out(const DecodeArgs &a, hipStream_t stream)
+{
+    return a.out_f32 ? launch_dim<T, float>(a, stream) : launch_dim<T, T>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream)
 {
-    if (a.elem_bytes == 4)
-        return launch_dim<float>(a, stream);
-    if (a.elem_bytes == 2)
-        return launch_dim<_Float16>(a, stream);
-    return hipErrorInvalidValue;
+    switch (a.dtype) {
+    case kDtypeF32: return launch_dim<float, float>(a, stream);
+    case kDtypeF16: return launch_out<_Float16>(a, stream);
+    case kDtypeBF16: return launch_out<__bf16>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace photon

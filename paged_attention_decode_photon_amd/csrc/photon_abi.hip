@@ -37,7 +37,19 @@ photon_status ok()
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int elem_bytes_of(int32_t dtype) { return dtype == PHOTON_F32 ? 4 : dtype == PHOTON_F16 ? 2 : 0; }
+int elem_bytes_of(int32_t dtype)
+{
+    switch (dtype) {
+    case PHOTON_F32: return 4;
+    case PHOTON_F16: return 2;
+    case PHOTON_BF16: return 2;
+    default: return 0;
+    }
+}
+static_assert(PHOTON_F32 == photon::kDtypeF32 && PHOTON_F16 == photon::kDtypeF16 &&
+                  PHOTON_BF16 == photon::kDtypeBF16,
+              "dtype codes");
+constexpr int32_t kKnownDecodeFlags = PHOTON_DECODE_OUT_F32;
 
 // Default number of decode wavefronts: enough per compute unit of an MI355X
 // (256 CUs) that the units being read, one per wave, add up to 64 KiB in
@@ -97,6 +109,8 @@ photon_status plan_decode(const photon_decode_desc *d, Plan *plan)
                     "max_context_len=%d partition_tokens=%d)",
                     d->num_seqs, d->num_q_heads, d->max_blocks_per_seq, d->max_context_len,
                     d->partition_tokens);
+    if (d->flags & ~kKnownDecodeFlags)
+        return fail(PHOTON_ERR_INVALID_ARG, "unknown decode flags 0x%x", (unsigned)d->flags);
     if (d->num_q_heads % d->kv.num_kv_heads != 0)
         return fail(PHOTON_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
                     d->num_q_heads, d->kv.num_kv_heads);
@@ -247,6 +261,8 @@ photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const
     a.group = p.group;
     a.head_dim = desc->kv.head_dim;
     a.elem_bytes = p.elem_bytes;
+    a.dtype = desc->kv.dtype;
+    a.out_f32 = (desc->flags & PHOTON_DECODE_OUT_F32) ? 1 : 0;
     a.max_blocks = desc->max_blocks_per_seq;
     a.num_waves = p.num_waves;
     a.qscale = (float)((double)scale * 1.4426950408889634);  // log2(e)

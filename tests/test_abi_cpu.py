@@ -6,6 +6,7 @@ library guarantees happens before its first HIP call.
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -48,8 +49,28 @@ def kv(nb=64, hkv=8, bs=16, d=64, dtype=pa.F32):
     return pa.KvDesc(nb, hkv, bs, d, dtype)
 
 
-def dd(b=16, hq=32, mb=128, maxctx=2048, part=0, **kw):
-    return pa.DecodeDesc(b, hq, mb, maxctx, part, kv(**kw))
+def dd(b=16, hq=32, mb=128, maxctx=2048, part=0, flags=0, **kw):
+    return pa.DecodeDesc(b, hq, mb, maxctx, part, kv(**kw), flags)
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    # Compile the header with the host C compiler and compare the layout of
+    # both descriptors with the ctypes mirrors the binding passes.
+    prog = tmp_path / "layout.c"
+    prog.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "photon_decode.h"\n'
+        "int main(void) {\n"
+        '  printf("%zu %zu %zu %zu %zu %d %d\\n", sizeof(photon_kv_desc), sizeof(photon_decode_desc),\n'
+        "         offsetof(photon_decode_desc, kv), offsetof(photon_decode_desc, flags),\n"
+        "         offsetof(photon_kv_desc, dtype), PHOTON_BF16, PHOTON_DECODE_OUT_F32);\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), "-o", str(exe),
+                           str(prog)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    assert got == [ctypes.sizeof(pa.KvDesc), ctypes.sizeof(pa.DecodeDesc),
+                   pa.DecodeDesc.kv.offset, pa.DecodeDesc.flags.offset, pa.KvDesc.dtype.offset,
+                   pa.BF16, pa.DECODE_OUT_F32]
 
 
 def write(desc, n=4, k=FAKE, v=FAKE, slots=FAKE, kc=FAKE, vc=FAKE):
@@ -95,6 +116,10 @@ def test_partition_quantum_and_auto_size():
     # fp16 / d128 / group 2
     assert pa.lib.photon_paged_attn_partition_quantum(
         ctypes.byref(dd(hq=16, d=128, dtype=pa.F16))) == 32
+    # bf16 rows are as wide as fp16 rows, with or without fp32 output
+    for flags in (0, pa.DECODE_OUT_F32):
+        assert pa.lib.photon_paged_attn_partition_quantum(
+            ctypes.byref(dd(dtype=pa.BF16, flags=flags))) == 32
     # auto: 16 seqs x 8 KV heads x 64 units = 8192 units over 1024 waves
     assert pa.lib.photon_paged_attn_partition_tokens(ctypes.byref(dd())) == 8 * 32
     # 3 units per wave -> 2731 waves, rounded up to whole workgroups
@@ -123,6 +148,9 @@ def test_workspace_size_formula():
     (dd(b=-1), pa.ERR_INVALID_ARG),
     (dd(b=2049), pa.ERR_UNSUPPORTED),
     (dd(bs=32), pa.ERR_UNSUPPORTED),
+    (dd(flags=2), pa.ERR_INVALID_ARG),          # unknown flag bit
+    (dd(flags=-1), pa.ERR_INVALID_ARG),
+    (dd(dtype=3), pa.ERR_INVALID_ARG),
 ])
 def test_decode_rejects_bad_descriptor(desc, code):
     n = ctypes.c_size_t(0)

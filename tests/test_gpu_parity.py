@@ -1,8 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
 
-Tolerances (max-abs on every output element): 1e-4 for fp32 storage and
-2e-3 for fp16 storage with fp32 accumulation.  Cache writes must be
-bit-exact over the whole pool.  The oracle runs first on every input set,
+Tolerances (on every output element, fp32 accumulation throughout): max-abs
+1e-4 for fp32 output (fp32 storage, or 16-bit storage with the fp32-output
+flag: the inputs are exact in both); 2e-3 for fp16 output (half an fp16 ulp
+of |o| < 4, plus the accumulation); for bfloat16 output 1e-4 + 2^-8 |ref|,
+since rounding to nearest in bfloat16 (8 significant bits) moves a value by
+at most 2^-8 of itself.  Cache writes must be bit-exact over the whole pool.  The oracle runs first on every input set,
 so its precondition checks (slot and block-id ranges, context bounds) guard
 each launch.
 """
@@ -16,6 +19,13 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 TOL = {np.dtype(np.float32): 1e-4, np.dtype(np.float16): 2e-3}
+DTYPES = [np.float32, np.float16, di.BF16]
+
+
+def tolerance(out_dtype, ref):
+    if np.dtype(out_dtype) == di.BF16:
+        return 1e-4 + 2.0 ** -8 * np.abs(ref)
+    return TOL[np.dtype(out_dtype)]
 
 
 @pytest.fixture(scope="module")
@@ -26,26 +36,27 @@ def pa():
 
 
 def dev(a):
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    return di.to_torch(a).to("cuda:0")
 
 
 def host(t):
-    return t.detach().cpu().numpy()
+    return di.from_torch(t)
 
 
-def gpu_decode(pa, q, kc, vc, tables, ctx, scale, max_ctx=None, part=0):
+def gpu_decode(pa, q, kc, vc, tables, ctx, scale, max_ctx=None, part=0, out_dtype=None):
     out = pa.paged_attn_decode(dev(q), dev(kc), dev(vc), dev(tables), dev(ctx), scale,
                                max_context_len=int(ctx.max()) if max_ctx is None else max_ctx,
-                               partition_tokens=part)
+                               partition_tokens=part, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return host(out)
 
 
 def assert_close(got, ref, dtype, what=""):
-    err = np.abs(got.astype(np.float64) - ref)
+    g = di.as_float64(got)
+    err = np.abs(g - ref)
     worst = float(np.nanmax(err)) if err.size else 0.0
-    assert np.isfinite(got).all(), f"{what}: non-finite output"
-    assert worst <= TOL[np.dtype(dtype)], f"{what}: max-abs error {worst:.3e}"
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    assert (err <= tolerance(dtype, ref)).all(), f"{what}: max-abs error {worst:.3e}"
     return worst
 
 
@@ -62,24 +73,25 @@ def random_case(rng, dtype, b, hq, hkv, d, ctx_list=None, max_ctx=64, spare=3):
     for i, n in enumerate(need):
         tables[i, :n] = perm[p:p + n]
         p += n
-    q = rng.standard_normal((b, hq, d)).astype(dtype)
-    kc = rng.standard_normal((nb, hkv, 16, d)).astype(dtype)
-    vc = rng.standard_normal((nb, hkv, 16, d)).astype(dtype)
+    q = di.cast(rng.standard_normal((b, hq, d)), dtype)
+    kc = di.cast(rng.standard_normal((nb, hkv, 16, d)), dtype)
+    vc = di.cast(rng.standard_normal((nb, hkv, 16, d)), dtype)
     return q, kc, vc, tables, ctx
 
 
 # ----------------------------------------------------------------- cache write
 
 @pytest.mark.parametrize("dtype,hkv,d", [(np.float32, 8, 64), (np.float16, 8, 64),
-                                         (np.float16, 8, 128), (np.float32, 2, 128)])
+                                         (np.float16, 8, 128), (np.float32, 2, 128),
+                                         (di.BF16, 8, 64), (di.BF16, 8, 128)])
 def test_cache_write_bit_exact(pa, dtype, hkv, d):
     rng = np.random.default_rng(20)
     nb, t = 300, 77
-    kc = rng.standard_normal((nb, hkv, 16, d)).astype(dtype)
-    vc = rng.standard_normal((nb, hkv, 16, d)).astype(dtype)
-    k = rng.standard_normal((t, hkv, d)).astype(dtype)
-    v = rng.standard_normal((t, hkv, d)).astype(dtype)
-    if dtype == np.float16:  # NaN payloads, infinities and subnormals must survive
+    kc = di.cast(rng.standard_normal((nb, hkv, 16, d)), dtype)
+    vc = di.cast(rng.standard_normal((nb, hkv, 16, d)), dtype)
+    k = di.cast(rng.standard_normal((t, hkv, d)), dtype)
+    v = di.cast(rng.standard_normal((t, hkv, d)), dtype)
+    if np.dtype(dtype).itemsize == 2:  # NaN payloads, infinities and subnormals must survive
         k.view(np.uint16)[0, 0, :8] = [0x7E01, 0xFC00, 0x0001, 0x8001, 0x7C00, 0x7D55, 0xFFFF, 0x03FF]
     slots = di.random_injective_slots(nb, 16, t, rng, pad_fraction=0.15)
     ek, ev = oracle.kv_cache_write(k, v, slots, kc, vc)
@@ -103,7 +115,8 @@ def test_cache_write_all_padding_is_noop(pa):
 # ------------------------------------------------------------ decode vs oracle
 
 @pytest.mark.parametrize("name,layer", [("tiny", 0), ("llama1b_b1", 0), ("llama1b_b16", 0),
-                                        ("llama1b_b16", 11), ("cb_b64", 0)])
+                                        ("llama1b_b16", 11), ("cb_b64", 0),
+                                        ("llama1b_b16_bf16", 0), ("llama1b_b16_bf16", 15)])
 def test_decode_matches_oracle_on_workloads(pa, name, layer):
     cfg = di.CONFIGS[name]
     lay = di.make_layout(cfg)
@@ -129,7 +142,7 @@ def test_decode_qwen3_long_sampled(pa):
         print(f"qwen3_long seq {b}: max-abs {err:.3e}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "cb_b64"])
+@pytest.mark.parametrize("name", ["tiny", "cb_b64", "llama1b_b16_bf16"])
 def test_decode_step_writes_then_attends(pa, name):
     # The step writes each sequence's new K/V at logical position ctx-1 and
     # then attends over all ctx tokens, the new one included.
@@ -147,7 +160,7 @@ def test_decode_step_writes_then_attends(pa, name):
     assert_close(host(out), ref, cfg.np_dtype, name)
 
 
-@pytest.mark.parametrize("name", ["tiny", "cb_b64"])
+@pytest.mark.parametrize("name", ["tiny", "cb_b64", "llama1b_b16_bf16"])
 def test_unread_slots_never_reach_the_output(pa, name):
     cfg = di.CONFIGS[name]
     lay = di.make_layout(cfg, num_blocks=None)
@@ -157,7 +170,7 @@ def test_unread_slots_never_reach_the_output(pa, name):
     kp = di.poison_unused(cfg, lay, t.k_cache)
     vp = di.poison_unused(cfg, lay, t.v_cache)
     poisoned = gpu_decode(pa, t.q, kp, vp, *args)
-    assert np.isfinite(poisoned).all()
+    assert np.isfinite(di.as_float64(poisoned)).all()
     assert poisoned.tobytes() == clean.tobytes()
 
 
@@ -176,7 +189,7 @@ def test_block_permutation_and_repeat_are_bit_identical(pa):
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", [(np.float32, 32, 8, 64), (np.float16, 32, 8, 64),
-                                            (np.float16, 16, 8, 128)])
+                                            (np.float16, 16, 8, 128), (di.BF16, 32, 8, 64)])
 def test_partition_sizes_agree_with_oracle(pa, dtype, hq, hkv, d):
     rng = np.random.default_rng(23)
     q, kc, vc, tables, ctx = random_case(rng, dtype, 6, hq, hkv, d,
@@ -191,11 +204,11 @@ def test_partition_sizes_agree_with_oracle(pa, dtype, hq, hkv, d):
         assert_close(got, ref, dtype, f"partition {part}")
 
 
-@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_every_built_shape(pa, dtype, d, group):
-    rng = np.random.default_rng(1000 + group * 10 + d + (dtype == np.float16))
+    rng = np.random.default_rng(1000 + group * 10 + d + DTYPES.index(dtype))
     hkv = 2
     ctx = [0, 1, 15, 16, 17, 31, 33, 64, 100, 333]
     q, kc, vc, tables, ctx = random_case(rng, dtype, len(ctx), hkv * group, hkv, d, ctx_list=ctx)
@@ -203,7 +216,25 @@ def test_every_built_shape(pa, dtype, d, group):
     for part in (0, 64):
         got = gpu_decode(pa, q, kc, vc, tables, ctx, float(np.float32(d ** -0.5)), part=part)
         assert_close(got, ref, dtype, f"G{group} d{d} part {part}")
-        assert (got[0] == 0).all()  # empty context -> zero row
+        assert (di.as_float64(got[0]) == 0).all()  # empty context -> zero row
+
+
+@pytest.mark.parametrize("dtype", [np.float16, di.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_fp32_output_for_16bit_storage(pa, dtype, d, group):
+    # The fp32-output kernels skip the final rounding: fp32 tolerance applies.
+    rng = np.random.default_rng(2000 + group * 10 + d + DTYPES.index(dtype))
+    hkv = 2
+    ctx = [0, 1, 16, 17, 63, 200, 333, 1000]
+    q, kc, vc, tables, ctx = random_case(rng, dtype, len(ctx), hkv * group, hkv, d, ctx_list=ctx)
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, float(np.float32(d ** -0.5)))
+    for part in (0, 64):
+        got = gpu_decode(pa, q, kc, vc, tables, ctx, float(np.float32(d ** -0.5)), part=part,
+                         out_dtype=torch.float32)
+        assert got.dtype == np.float32
+        assert_close(got, ref, np.float32, f"fp32 out G{group} d{d} part {part}")
+        assert (got[0] == 0).all()
 
 
 def test_context_edges_around_partition_boundaries(pa):

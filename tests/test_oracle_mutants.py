@@ -34,7 +34,13 @@ MUTANTS = {
     "q_batch_index_dropped": ("widen(q, pair * head_dim + j, dtype)", "widen(q, h * head_dim + j, dtype)"),
     "half_bias_off_by_one": ("expo - 25", "expo - 24"),
     "half_subnormal_scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -23)"),
-    "half_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
+    "half_sign_dropped": ("mag = ldexp((double)(frac | 0x400), expo - 25);\n    return sign ? -mag : mag;",
+                          "mag = ldexp((double)(frac | 0x400), expo - 25);\n    return mag;"),
+    "bf16_bias_off_by_one": ("expo - 134", "expo - 133"),
+    "bf16_fraction_bits": ("const int frac = bits & 0x7f;", "const int frac = bits & 0x3f;"),
+    "bf16_subnormal_scale": ("ldexp((double)frac, -133)", "ldexp((double)frac, -126)"),
+    "bf16_read_as_half": ("return oracle_bfloat16_to_double(((const uint16_t *)base)[idx]);",
+                          "return oracle_half_to_double(((const uint16_t *)base)[idx]);"),
     "write_head_block_transposed": ("((blk * num_kv_heads + h) * block_size + off)",
                                     "((h * num_blocks + blk) * block_size + off)"),
     "write_offset_swapped": ("const int64_t off = s % block_size;", "const int64_t off = s / block_size % block_size;"),
@@ -55,6 +61,7 @@ def _pin_suite():
         ("dominant_key", pins.test_dominant_key_selects_its_value, (1000.0,)),
         ("empty_ctx", pins.test_empty_context_gives_zero_row, ()),
         ("half_all", pins.test_half_decoder_matches_numpy_on_all_bit_patterns, ()),
+        ("bf16_all", pins.test_bfloat16_decoder_matches_torch_on_all_bit_patterns, ()),
         ("write_brute_f16", pins.test_cache_write_brute_force, (np.float16,)),
         ("preconditions", pins.test_precondition_errors, ()),
     ] + [(f"sdpa_{s}", pins.test_matches_torch_sdpa_float64, (np.float32, s)) for s in range(3)]

@@ -3,7 +3,8 @@
 Each test pins the oracle to something fixed by the mathematics or by a
 library routine that the oracle does not use: hand-worked golden cases,
 dense attention via torch's scaled_dot_product_attention, closed forms,
-invariances, and exhaustive decoding of binary16.
+invariances, and exhaustive decoding of binary16 and bfloat16 (against
+numpy's and torch's own conversions).
 """
 import json
 import math
@@ -81,11 +82,11 @@ def _dense_sdpa(q, kc, vc, tables, ctx, scale):
         if c == 0:
             continue
         t = np.arange(c)
-        k = kc[tables[i, t // bs], :, t % bs, :].astype(np.float64)  # [c, Hkv, d]
-        v = vc[tables[i, t // bs], :, t % bs, :].astype(np.float64)
+        k = di.as_float64(kc[tables[i, t // bs], :, t % bs, :])  # [c, Hkv, d]
+        v = di.as_float64(vc[tables[i, t // bs], :, t % bs, :])
         kt = torch.from_numpy(np.ascontiguousarray(np.repeat(k.transpose(1, 0, 2), grp, axis=0)))
         vt = torch.from_numpy(np.ascontiguousarray(np.repeat(v.transpose(1, 0, 2), grp, axis=0)))
-        qt = torch.from_numpy(q[i].astype(np.float64)[:, None, :])
+        qt = torch.from_numpy(di.as_float64(q[i])[:, None, :])
         o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=float(scale))
         out[i] = o[:, 0, :].numpy()
     return out
@@ -103,13 +104,13 @@ def _random_case(rng, dtype, b, hq, hkv, d, bs, max_ctx, spare=2):
     for i, n in enumerate(need):
         tables[i, :n] = perm[p:p + n]
         p += n
-    q = rng.standard_normal((b, hq, d)).astype(dtype)
-    kc = rng.standard_normal((nb, hkv, bs, d)).astype(dtype)
-    vc = rng.standard_normal((nb, hkv, bs, d)).astype(dtype)
+    q = di.cast(rng.standard_normal((b, hq, d)), dtype)
+    kc = di.cast(rng.standard_normal((nb, hkv, bs, d)), dtype)
+    vc = di.cast(rng.standard_normal((nb, hkv, bs, d)), dtype)
     return q, kc, vc, tables, ctx
 
 
-@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16, di.BF16])
 @pytest.mark.parametrize("seed", range(6))
 def test_matches_torch_sdpa_float64(dtype, seed):
     rng = np.random.default_rng(100 + seed)
@@ -142,12 +143,12 @@ def _single_seq(rng, dtype, ctx, hq=4, hkv=2, d=16, bs=4):
     return q, kc, vc, tables, np.array([ctx], np.int32)
 
 
-@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16, di.BF16])
 def test_one_token_returns_its_value_row(dtype):
     rng = np.random.default_rng(7)
     q, kc, vc, tables, ctx = _single_seq(rng, dtype, 1)
     out = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.3)
-    v0 = vc[tables[0, 0], :, 0, :].astype(np.float64)  # [Hkv, d]
+    v0 = di.as_float64(vc[tables[0, 0], :, 0, :])  # [Hkv, d]
     np.testing.assert_array_equal(out[0], np.repeat(v0, 2, axis=0))
 
 
@@ -198,7 +199,7 @@ def test_empty_context_gives_zero_row():
 
 # ---------------------------------------------------------------- invariances
 
-@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16, di.BF16])
 def test_physical_block_permutation_is_bit_identical(dtype):
     rng = np.random.default_rng(12)
     q, kc, vc, tables, ctx = _random_case(rng, dtype, 4, 8, 2, 16, 4, 45, spare=5)
@@ -245,6 +246,7 @@ def test_unread_slots_never_reach_the_output():
     kp = di.poison_unused(cfg, lay, t.k_cache)
     vp = di.poison_unused(cfg, lay, t.v_cache)
     assert np.isnan(kp).sum() > 0
+    assert np.isnan(di.as_float64(kp)).sum() == np.isnan(kp).sum()
     got = oracle.paged_attn_decode(t.q, kp, vp, lay.block_tables, lay.context_lens, cfg.scale)
     assert np.array_equal(got, ref)
 
@@ -274,16 +276,51 @@ def test_half_decoder_matches_numpy_on_all_bit_patterns():
         assert oracle.half_to_double(b) == float(np.uint16(b).view(np.float16))
 
 
+# ------------------------------------------------------------- bfloat16
+
+def test_bfloat16_decoder_matches_torch_on_all_bit_patterns():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    d = 64
+    vals = bits.view(di.BF16).reshape(-1, d)
+    n = vals.shape[0]
+    vc = np.ascontiguousarray(vals.reshape(n, 1, 1, d))
+    kc = np.zeros(vc.shape, np.uint16).view(di.BF16)
+    q = np.zeros((n, 1, d), np.uint16).view(di.BF16)
+    tables = np.arange(n, dtype=np.int32).reshape(n, 1)
+    ctx = np.ones(n, np.int32)
+    got = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 1.0).reshape(-1)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # the scalar entry point: zero, subnormals, one, the largest finite, infinities
+    for b, v in [(0x0000, 0.0), (0x0001, 2.0 ** -133), (0x007F, 127 * 2.0 ** -133),
+                 (0x0080, 2.0 ** -126), (0x3F80, 1.0), (0xBFC0, -1.5),
+                 (0x7F7F, (2 - 2.0 ** -7) * 2.0 ** 127), (0x7F80, math.inf), (0xFF80, -math.inf)]:
+        assert oracle.bfloat16_to_double(b) == v
+    assert math.isnan(oracle.bfloat16_to_double(0x7FC0))
+
+
+def test_bfloat16_rounding_of_inputs_matches_torch():
+    # The input generator rounds float32 draws to bfloat16 itself; torch's
+    # float32 -> bfloat16 conversion (round to nearest even) must agree.
+    x = np.random.default_rng(16).standard_normal(1 << 16).astype(np.float32)
+    x[:6] = [1.00390625, 1.01171875, -1.00390625, 3.0e38, 1e-39, 0.0]  # ties and edges
+    got = di.to_storage(x, di.BF16).view(np.uint16)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
 # ------------------------------------------------------------- cache write
 
-@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16, di.BF16])
 def test_cache_write_brute_force(dtype):
     rng = np.random.default_rng(15)
     nb, hkv, bs, d, t = 12, 3, 16, 64, 40
-    kc = rng.standard_normal((nb, hkv, bs, d)).astype(dtype)
-    vc = rng.standard_normal((nb, hkv, bs, d)).astype(dtype)
-    k = rng.standard_normal((t, hkv, d)).astype(dtype)
-    v = rng.standard_normal((t, hkv, d)).astype(dtype)
+    kc = di.cast(rng.standard_normal((nb, hkv, bs, d)), dtype)
+    vc = di.cast(rng.standard_normal((nb, hkv, bs, d)), dtype)
+    k = di.cast(rng.standard_normal((t, hkv, d)), dtype)
+    v = di.cast(rng.standard_normal((t, hkv, d)), dtype)
     slots = di.random_injective_slots(nb, bs, t, rng, pad_fraction=0.2)
     assert (slots == -1).any()
     nk, nv = oracle.kv_cache_write(k, v, slots, kc, vc)
