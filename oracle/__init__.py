@@ -7,6 +7,10 @@ The arithmetic lives in ``photon_oracle.c`` (plain C, fp64, optional OpenMP
 over independent (sequence, head) pairs); this module builds it with gcc and
 wraps it with ctypes, marshalling numpy arrays only.
 
+Rotary embedding (``rope``, ``rope_kv_cache_write``) is pinned against
+transformers' GPT-J and Llama rotary routines and against the rotation
+group's identities (see ``tests/test_oracle_rope.py``).
+
 Parity pins (all in ``tests/test_oracle_*.py``): hand-derived golden cases,
 dense attention through ``torch.nn.functional.scaled_dot_product_attention``,
 closed forms (one token, constant V, zero query, dominant key), invariance
@@ -72,6 +76,11 @@ def _configure(lib):
                                              i64, ctypes.c_int, ctypes.c_double, vp, vp,
                                              ctypes.c_int]
     lib.oracle_paged_attn_decode.restype = ctypes.c_int
+    lib.oracle_rope.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                vp]
+    lib.oracle_rope.restype = ctypes.c_int
+    lib.oracle_widen.argtypes = [vp, i64, ctypes.c_int, vp]
+    lib.oracle_widen.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -172,3 +181,53 @@ def paged_attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     if rc != OK:
         raise OracleError(rc, "paged_attn_decode")
     return (out, probs) if return_probs else out
+
+
+def _code(a: np.ndarray) -> int:
+    if a.dtype not in _DTYPE_CODE:
+        raise OracleError(ERR_ARG, f"dtype {a.dtype}")
+    return _DTYPE_CODE[a.dtype]
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    """Exact float64 values of a float32 / float16 / bfloat16 storage array."""
+    a = np.ascontiguousarray(a)
+    out = np.empty(a.shape, dtype=np.float64)
+    rc = _load().oracle_widen(_ptr(a), a.size, _code(a), _ptr(out))
+    if rc != OK:
+        raise OracleError(rc, "widen")
+    return out
+
+
+def rope(x: np.ndarray, positions: np.ndarray, base: float, interleaved: bool = False) -> np.ndarray:
+    """fp64 rotary embedding of x [T, H, D] at ``positions`` [T] (see photon_oracle.c)."""
+    x = np.ascontiguousarray(x)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    t, h, d = x.shape
+    if pos.shape != (t,):
+        raise OracleError(ERR_ARG, "positions shape")
+    out = np.full(x.shape, np.nan, dtype=np.float64)
+    rc = _load().oracle_rope(_ptr(x), _ptr(pos), t, h, d, _code(x), float(base), int(interleaved),
+                             _ptr(out))
+    if rc != OK:
+        raise OracleError(rc, "rope")
+    return out
+
+
+def rope_kv_cache_write(q, k, v, positions, slot_mapping, k_cache, v_cache, base: float,
+                        interleaved: bool = False):
+    """Rotary embedding of q and k, then the slot-mapped write of rotated k and raw v.
+
+    Returns (q_out [T, Hq, D] float64, k_cache as float64 with the rotated rows
+    of written slots in place, v_cache in the pool dtype after a raw-byte
+    write).  Slot checks are those of :func:`kv_cache_write`.
+    """
+    q_out = rope(q, positions, base, interleaved)
+    k_rot = rope(k, positions, base, interleaved)
+    _, v_new = kv_cache_write(k, v, slot_mapping, k_cache, v_cache)
+    k_new = widen(k_cache)
+    bs = k_cache.shape[2]
+    for i, s in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if s >= 0:
+            k_new[s // bs, :, s % bs, :] = k_rot[i]
+    return q_out, k_new, v_new

@@ -6,7 +6,8 @@
  *
  * What it follows (PhotonInfer README, zh-CN / fr / ja translations):
  *   - "GPU-optimised kernels": batched paged attention over a block-level KV
- *     cache, and a numerically stable softmax;
+ *     cache, a numerically stable softmax, and batched RoPE among the fused
+ *     operations;
  *   - "Technical details -> Paged attention": a block-level KV cache, per
  *     sequence cache offsets (read as block tables), and one batched K/V
  *     write for many sequences (read as a per-token slot mapping).
@@ -241,6 +242,60 @@ int oracle_paged_attn_decode(const void *q, const void *k_cache, const void *v_c
         free(s);
     }
     return rc;
+}
+
+/* Rotary position embedding (the README's "GPU-optimised kernels" section
+ * lists batched RoPE among its fused operations; the rotation itself is the
+ * textbook one of RoFormer).  Each head row x of token i is split into D/2
+ * pairs; pair j is rotated by the angle positions[i] * base^(-2j/D):
+ *   x'_a = x_a cos(angle) - x_b sin(angle),  x'_b = x_a sin(angle) + x_b cos(angle).
+ * Pair j is (x_j, x_{j+D/2}) when interleaved == 0 (the rotate-half layout of
+ * Llama / GPT-NeoX), and (x_{2j}, x_{2j+1}) when interleaved == 1 (the layout
+ * of the RoFormer paper and GPT-J).
+ *   x    [T, H, D] dtype (widened exactly)
+ *   out  [T, H, D] double
+ * Angles, sines, cosines and the rotation are all formed in double. */
+int oracle_rope(const void *x, const int32_t *positions, int64_t num_tokens, int64_t num_heads,
+                int64_t head_dim, int dtype, double base, int interleaved, double *out)
+{
+    if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || head_dim % 2 != 0 ||
+        !(base > 0.0) || (interleaved != 0 && interleaved != 1) ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+        return ORACLE_ERR_ARG;
+    if (num_tokens == 0)
+        return ORACLE_OK;
+    if (!x || !positions || !out)
+        return ORACLE_ERR_ARG;
+    const int64_t half = head_dim / 2;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        if (positions[i] < 0)
+            return ORACLE_ERR_ARG;
+        for (int64_t j = 0; j < half; ++j) {
+            const double angle = (double)positions[i] * pow(base, -2.0 * (double)j / (double)head_dim);
+            const double c = cos(angle), s = sin(angle);
+            const int64_t ia = interleaved ? 2 * j : j;
+            const int64_t ib = interleaved ? 2 * j + 1 : j + half;
+            for (int64_t h = 0; h < num_heads; ++h) {
+                const int64_t row = (i * num_heads + h) * head_dim;
+                const double xa = widen(x, row + ia, dtype);
+                const double xb = widen(x, row + ib, dtype);
+                out[row + ia] = xa * c - xb * s;
+                out[row + ib] = xa * s + xb * c;
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Exact double values of n storage elements. */
+int oracle_widen(const void *x, int64_t n, int dtype, double *out)
+{
+    if (n < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
+        (n > 0 && (!x || !out)))
+        return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = widen(x, i, dtype);
+    return ORACLE_OK;
 }
 
 int oracle_max_threads(void)

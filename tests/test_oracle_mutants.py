@@ -2,8 +2,9 @@
 
 Each case plants one mistake into a temporary copy of the oracle's C source
 (a dropped term, a wrong index or sign, a transposed operand), builds it on
-the CPU and runs the pin suite against it: at least one pin has to fail.
-The unmodified source must pass the same suite.
+the CPU and runs the pin suite against it: at least one pin has to fail (or
+the build must crash on them).  The unmodified source must pass the same
+suite.
 """
 import os
 import subprocess
@@ -14,6 +15,7 @@ import pytest
 
 import oracle
 import tests.test_oracle_pins as pins
+import tests.test_oracle_rope as rp
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "photon_oracle.c")
 
@@ -46,6 +48,15 @@ MUTANTS = {
     "write_offset_swapped": ("const int64_t off = s % block_size;", "const int64_t off = s / block_size % block_size;"),
     "write_v_from_k": ("(const char *)v + src", "(const char *)k + src"),
     "no_duplicate_check": ("if (seen[s]) {", "if (0) {"),
+    "rope_sign": ("out[row + ia] = xa * c - xb * s;", "out[row + ia] = xa * c + xb * s;"),
+    "rope_frequency_exponent": ("pow(base, -2.0 * (double)j / (double)head_dim)",
+                                "pow(base, -1.0 * (double)j / (double)head_dim)"),
+    "rope_pairing": ("const int64_t ib = interleaved ? 2 * j + 1 : j + half;",
+                     "const int64_t ib = interleaved ? 2 * j + 1 : head_dim - 1 - j;"),
+    "rope_position_off_by_one": ("const double angle = (double)positions[i] *",
+                                 "const double angle = (double)(positions[i] + 1) *"),
+    "rope_sin_cos_swapped": ("const double c = cos(angle), s = sin(angle);",
+                             "const double c = sin(angle), s = cos(angle);"),
     "empty_ctx_not_zeroed": ("memset(o, 0, sizeof(double) * (size_t)head_dim);\n            continue;",
                              "continue;"),
 }
@@ -64,6 +75,9 @@ def _pin_suite():
         ("bf16_all", pins.test_bfloat16_decoder_matches_torch_on_all_bit_patterns, ()),
         ("write_brute_f16", pins.test_cache_write_brute_force, (np.float16,)),
         ("preconditions", pins.test_precondition_errors, ()),
+        ("rope_gptj", rp.test_adjacent_pairs_match_transformers_gptj, (np.float32,)),
+        ("rope_llama", rp.test_rotate_half_matches_transformers_llama, (64,)),
+        ("rope_identities", rp.test_rotation_identities, (False,)),
     ] + [(f"sdpa_{s}", pins.test_matches_torch_sdpa_float64, (np.float32, s)) for s in range(3)]
     for name, fn, args in checks:
         try:
@@ -73,43 +87,72 @@ def _pin_suite():
     return failures
 
 
-def _build_variant(tmp_path, text, tag):
-    src = tmp_path / f"oracle_{tag}.c"
-    lib = tmp_path / f"liboracle_{tag}.so"
-    src.write_text(text)
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w",
-                           "-o", str(lib), str(src), "-lm"])
-    return str(lib)
+def _build_variant(dirpath, text, tag):
+    src = os.path.join(dirpath, f"oracle_{tag}.c")
+    lib = os.path.join(dirpath, f"liboracle_{tag}.so")
+    with open(src, "w") as f:
+        f.write(text)
+    return src, lib, subprocess.Popen(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w",
+                                       "-o", lib, src, "-lm"])
 
 
-def _run_suite_in_child(lib):
-    """Run the pin suite against ``lib`` in a child process.
+_CHILD = """
+import sys, oracle, tests.test_oracle_mutants as m
+for tag, lib in zip(sys.argv[1::2], sys.argv[2::2]):
+    print('START', tag, flush=True)
+    with oracle.use_library(lib):
+        f = m._pin_suite()
+    print('RESULT', tag, len(f), flush=True)
+"""
 
-    A mutant may index outside its arrays and crash; a crash counts as a
-    rejection, so the child keeps that from taking the test run down.
-    Returns (exit status, printed failures).
+
+def _run_suites(items):
+    """Run the pin suite against each (tag, lib) in child processes.
+
+    One child runs them in turn (importing the pins once).  A mutant may
+    index outside its arrays and crash its child: a crash counts as a
+    rejection of that mutant, and a new child goes on with the rest.
+    Returns {tag: number of failing pins, or -1 for a crash}.
     """
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    code = ("import sys, oracle, tests.test_oracle_mutants as m\n"
-            f"with oracle.use_library({lib!r}):\n"
-            "    f = m._pin_suite()\n"
-            "print('FAILURES', len(f), f)\n")
-    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
-                       timeout=300, env={**os.environ, "OMP_NUM_THREADS": "2"})
-    return r.returncode, r.stdout.strip().splitlines()[-1] if r.stdout.strip() else ""
+    results, todo = {}, list(items)
+    while todo:
+        args = [x for item in todo for x in item]
+        r = subprocess.run([sys.executable, "-c", _CHILD, *args], cwd=root, capture_output=True,
+                           text=True, timeout=900, env={**os.environ, "OMP_NUM_THREADS": "2"})
+        started = None
+        for line in r.stdout.splitlines():
+            parts = line.split()
+            if parts[:1] == ["START"]:
+                started = parts[1]
+            elif parts[:1] == ["RESULT"]:
+                results[parts[1]] = int(parts[2])
+                started = None
+        if r.returncode != 0:
+            if started is None:
+                raise RuntimeError(f"mutation child failed outside a suite: {r.stderr[-2000:]}")
+            results[started] = -1
+        todo = [item for item in todo if item[0] not in results]
+    return results
 
 
-def test_unmodified_source_passes(tmp_path):
-    lib = _build_variant(tmp_path, open(SRC).read(), "clean")
-    rc, line = _run_suite_in_child(lib)
-    assert rc == 0 and line == "FAILURES 0 []", line
+@pytest.fixture(scope="module")
+def suite_results(tmp_path_factory):
+    d = str(tmp_path_factory.mktemp("mutants"))
+    text = open(SRC).read()
+    builds = {"clean": _build_variant(d, text, "clean")}
+    for name, (old, new) in MUTANTS.items():
+        assert old in text, f"mutation anchor for {name} not found"
+        builds[name] = _build_variant(d, text.replace(old, new), name)
+    for tag, (_, _, proc) in builds.items():
+        assert proc.wait() == 0, f"build of {tag} failed"
+    return _run_suites([(tag, lib) for tag, (_, lib, _) in builds.items()])
+
+
+def test_unmodified_source_passes(suite_results):
+    assert suite_results["clean"] == 0
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_reject_mutant(tmp_path, name):
-    old, new = MUTANTS[name]
-    text = open(SRC).read()
-    assert old in text, f"mutation anchor for {name} not found"
-    lib = _build_variant(tmp_path, text.replace(old, new), name)
-    rc, line = _run_suite_in_child(lib)
-    assert rc != 0 or not line.startswith("FAILURES 0"), f"no pin rejects the '{name}' mutant"
+def test_pins_reject_mutant(suite_results, name):
+    assert suite_results[name] != 0, f"no pin rejects the '{name}' mutant"
