@@ -37,7 +37,8 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["paged_attention_decode_photon_amd/csrc/paged_decode.hip",
                   "paged_attention_decode_photon_amd/csrc/lane_ops.h",
-                  "paged_attention_decode_photon_amd/csrc/launch.h"]
+                  "paged_attention_decode_photon_amd/csrc/launch.h",
+                  "paged_attention_decode_photon_amd/csrc/elem.h"]
 
 
 def kernel_source_sha256() -> str:
@@ -78,6 +79,17 @@ def write_bytes(cfg: di.DecodeConfig, num_tokens: int, num_written: int) -> int:
     return 2 * num_tokens * row + 2 * num_written * row + 4 * num_tokens
 
 
+def rope_write_bytes(cfg: di.DecodeConfig, num_tokens: int, num_written: int) -> int:
+    """Algorithmic bytes of one fused rotary + cache-write call.
+
+    Reads q, k, v, positions and slots; writes rotated q and, for written
+    tokens, the rotated k and raw v rows.
+    """
+    qrow = cfg.num_q_heads * cfg.head_dim * cfg.elem_bytes
+    kvrow = cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+    return num_tokens * (2 * qrow + 2 * kvrow + 8) + 2 * num_written * kvrow
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +99,9 @@ def parse_args(argv=None):
     ap.add_argument("--partition-tokens", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--rope-prefill-tokens", type=int, default=4096,
+                    help="tokens of the large fused rotary + cache-write call timed after the "
+                         "step (0 skips the rotary measurements)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (default: the step is also captured in a "
                          "HIP graph and replayed, and value uses the replays)")
@@ -123,6 +138,88 @@ def cpu_baseline(cfg, lay, host_layers, budget_s: float):
         "sample": f"{done} decode calls (whole layers, all {len(lay.context_lens)} sequences) of "
                   f"the {cfg.name} workload, {t_total:.1f} s wall; cache write not included",
         "ms_per_layer": round(t_total / done * 1e3, 3),
+    }
+
+
+def rope_measurements(args, cfg, lay, layers, slots, device, stream):
+    """Time the fused rotary + cache-write kernel, outside the step.
+
+    Two sizes: the decode step's T = batch tokens, one call per layer,
+    replayed from a HIP graph (this size is launch-bound); and one
+    prefill-sized call of ``--rope-prefill-tokens`` tokens at consecutive
+    positions into distinct slots of the first layer's pools, repeated.
+    """
+    import paged_attention_decode_photon_amd as pa
+    import torch
+
+    def event():
+        return torch.cuda.Event(enable_timing=True)
+
+    positions = di.to_torch(lay.positions).to(device)
+    for L in layers:
+        L["qr"] = torch.empty_like(L["q"])
+
+    def burst():
+        for L in layers:
+            pa.rope_kv_cache_write(L["q"], L["k"], L["v"], positions, slots, L["kc"], L["vc"],
+                                   cfg.rope_base, q_out=L["qr"])
+
+    # A call this small takes less GPU time than its Python launch, so the
+    # layers' calls are captured once in a HIP graph and the replays timed.
+    burst()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        burst()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = event(), event()
+    a.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    decode_us = a.elapsed_time(b) * 1e3 / (args.steps * len(layers))
+    t_dec = len(lay.positions)
+    n_written = int((lay.slot_mapping >= 0).sum())
+
+    t = args.rope_prefill_tokens
+    L = layers[0]
+    nslots = L["kc"].shape[0] * L["kc"].shape[2]
+    if t > nslots:
+        t = nslots
+    rng = np.random.default_rng(cfg.seed + 1000)
+    q = di.to_torch(di.cast(rng.standard_normal((t, cfg.num_q_heads, cfg.head_dim)),
+                            cfg.np_dtype)).to(device)
+    k = di.to_torch(di.cast(rng.standard_normal((t, cfg.num_kv_heads, cfg.head_dim)),
+                            cfg.np_dtype)).to(device)
+    v = torch.empty_like(k).copy_(k)
+    pos = torch.arange(t, dtype=torch.int32, device=device)
+    sl = di.to_torch(rng.permutation(nslots)[:t].astype(np.int32)).to(device)
+    qr = torch.empty_like(q)
+    kc, vc = L["kc"].clone(), L["vc"].clone()
+    for _ in range(2):
+        pa.rope_kv_cache_write(q, k, v, pos, sl, kc, vc, cfg.rope_base, q_out=qr)
+    torch.cuda.synchronize()
+    reps = max(args.steps, 5)
+    a.record(stream)
+    for _ in range(reps):
+        pa.rope_kv_cache_write(q, k, v, pos, sl, kc, vc, cfg.rope_base, q_out=qr)
+    b.record(stream)
+    torch.cuda.synchronize()
+    prefill_us = a.elapsed_time(b) * 1e3 / reps
+    nbytes = rope_write_bytes(cfg, t, t)
+    return {
+        "kernel": "rope_kv_cache_write_kernel (rotate-half pairs)",
+        "rope_base": cfg.rope_base,
+        "decode_tokens": t_dec,
+        "decode_us_per_call": round(decode_us, 3),
+        "decode_bytes_per_call": rope_write_bytes(cfg, t_dec, n_written),
+        "prefill_tokens": t,
+        "prefill_us_per_call": round(prefill_us, 3),
+        "prefill_bytes_per_call": nbytes,
+        "prefill_gbps": round(nbytes / (prefill_us * 1e-6) / 1e9, 1),
     }
 
 
@@ -274,6 +371,9 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     single_us = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in single)
 
+    rope = rope_measurements(args, cfg, lay, layers, slots, device, stream) \
+        if args.rope_prefill_tokens > 0 else None
+
     per_decode = decode_bytes(cfg, lay.context_lens)
     n_written = int((lay.slot_mapping >= 0).sum())
     per_write = write_bytes(cfg, T, n_written)
@@ -330,6 +430,8 @@ def main(argv=None) -> int:
             "bytes_per_launch": per_decode,
         },
     }
+    if rope is not None:
+        result["rope_kv_cache_write"] = rope
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, lay, host_layers, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -23,7 +23,8 @@ Recipe (all draws from ``numpy.random.default_rng``):
   q, K pool, V pool, new k, new v, each ``standard_normal`` in float32 and
   then rounded to nearest (ties to even) in the storage dtype;
 * the decode-step slot of sequence b is the logical position ``ctx_b - 1``
-  (the new token is written first and then attended to).
+  (the new token is written first and then attended to), which is also the
+  position its q and k are rotated by.
 """
 from __future__ import annotations
 
@@ -122,6 +123,7 @@ class DecodeConfig:
     block_size: int = BLOCK_SIZE
     pool_blocks: int | None = None  # None: exactly the blocks the tables use
     force_first_ctx: int | None = None
+    rope_base: float = 500000.0  # rotary frequency base (Llama 3: 5e5, Qwen3: 1e6)
 
     @property
     def group(self) -> int:
@@ -156,7 +158,7 @@ CONFIGS: dict[str, DecodeConfig] = {
                            "loguniform", 1, 8192, force_first_ctx=1),
     # Qwen3-0.6B-shaped long context, fp16 KV, head_dim 128.
     "qwen3_long": DecodeConfig("qwen3_long", 4, 8, 16, 8, 128, "f16",
-                               "fixed", 32768, 32768),
+                               "fixed", 32768, 32768, rope_base=1e6),
     # The batch-16 Llama step with bfloat16 KV (same seed, contexts, tables).
     "llama1b_b16_bf16": DecodeConfig("llama1b_b16_bf16", 2, 16, 32, 8, 64, "bf16",
                                      "uniform", 64, 2048, layers=16),
@@ -191,6 +193,7 @@ class BatchLayout:
     context_lens: np.ndarray  # [B] int32
     block_tables: np.ndarray  # [B, max_blocks] int32, unused entries = -1
     slot_mapping: np.ndarray  # [B] int32, slot of logical position ctx-1
+    positions: np.ndarray     # [B] int32, position ctx-1 of the new token (0 if ctx is 0)
     num_blocks: int
     max_blocks_per_seq: int
 
@@ -223,7 +226,8 @@ def make_layout(cfg: DecodeConfig, context_lens: np.ndarray | None = None,
         if c > 0:
             t = int(c) - 1
             slots[b] = tables[b, t // cfg.block_size] * cfg.block_size + t % cfg.block_size
-    return BatchLayout(ctx.astype(np.int32), tables, slots, nb, mb)
+    positions = np.maximum(ctx.astype(np.int32) - 1, 0)
+    return BatchLayout(ctx.astype(np.int32), tables, slots, positions, nb, mb)
 
 
 @dataclasses.dataclass

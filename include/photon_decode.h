@@ -8,7 +8,8 @@
  *     sequence cache offsets (here: block tables), and one kernel that writes
  *     the K/V of many sequences at once (here: a per-token slot mapping);
  *   - "GPU-optimised kernels": batched paged attention with a numerically
- *     stable softmax.
+ *     stable softmax, and batched RoPE among the fused operations (applied
+ *     to q and k in the same kernel as the cache write).
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PHOTON_ABI_VERSION 2
+#define PHOTON_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define PHOTON_API __attribute__((visibility("default")))
@@ -129,6 +130,49 @@ typedef struct photon_decode_desc {
 PHOTON_API photon_status photon_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                                     int32_t num_tokens, void *k_cache, void *v_cache,
                                     const photon_kv_desc *kv, void *stream);
+
+/* Rotary embedding parameters of photon_rope_kv_cache_write. */
+typedef struct photon_rope_desc {
+    double base;            /* frequency base, finite and > 0 (10000 in the RoFormer
+                               paper, 500000 for Llama 3, 1000000 for Qwen3)        */
+    int32_t adjacent_pairs; /* 0: pair j is (x_j, x_{j+D/2}), the rotate-half layout
+                               of Llama and GPT-NeoX; 1: pair j is (x_{2j}, x_{2j+1}),
+                               the layout of the RoFormer paper and GPT-J            */
+    int32_t reserved;       /* must be 0                                            */
+} photon_rope_desc;
+
+/*
+ * Fused rotary position embedding and slot-mapped KV cache write (README
+ * "GPU-optimised kernels": batched RoPE among the fused operations;
+ * "Technical details -> Paged attention": one kernel writes the K/V rows of
+ * many sequences).  For every token i at position p = positions[i] and
+ * every pair j < D/2 of each head row of q and k, with
+ * angle = p * base^(-2j/D) (formed in double, then rounded to fp32):
+ *
+ *   x'_a = x_a cos(angle) - x_b sin(angle),  x'_b = x_a sin(angle) + x_b cos(angle)
+ *
+ * Rotated q rows go to q_out; when slot_mapping[i] >= 0 the rotated k rows
+ * and the raw v rows go to pool row (slot / block_size, h, slot % block_size)
+ * of k_cache and v_cache.  The rotation is fp32 and the result is rounded to
+ * nearest even in kv->dtype; v is copied bit-exactly.
+ *
+ *   q, q_out      [num_tokens, num_q_heads, head_dim]   kv->dtype, 16-byte aligned;
+ *                 q_out may equal q (in place), must not overlap it otherwise
+ *   k, v          [num_tokens, num_kv_heads, head_dim]  kv->dtype, 16-byte aligned
+ *   positions     [num_tokens] int32, >= 0
+ *   slot_mapping  [num_tokens] int32, as for photon_kv_cache_write
+ *   k_cache, v_cache  pools, updated in place, 16-byte aligned
+ *
+ * num_q_heads must be > 0.  num_tokens == 0 launches nothing.  Errors as for
+ * photon_kv_cache_write, plus PHOTON_ERR_INVALID_ARG for a bad rope
+ * descriptor.
+ */
+PHOTON_API photon_status photon_rope_kv_cache_write(const void *q, void *q_out, const void *k,
+                                                    const void *v, const int32_t *positions,
+                                                    const int32_t *slot_mapping, int32_t num_tokens,
+                                                    int32_t num_q_heads, void *k_cache,
+                                                    void *v_cache, const photon_kv_desc *kv,
+                                                    const photon_rope_desc *rope, void *stream);
 
 /*
  * Token granularity of partition_tokens: the tokens of one unit of work (a

@@ -58,6 +58,11 @@ class DecodeDesc(ctypes.Structure):
                 ("partition_tokens", ctypes.c_int32), ("kv", KvDesc), ("flags", ctypes.c_int32)]
 
 
+class RopeDesc(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_double), ("adjacent_pairs", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 def _hip_runtimes_mapped() -> set[str]:
     try:
         with open("/proc/self/maps") as f:
@@ -81,6 +86,9 @@ def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     st = ctypes.c_int
     lib.photon_kv_cache_write.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.POINTER(KvDesc), vp]
     lib.photon_kv_cache_write.restype = st
+    lib.photon_rope_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp,
+                                               ctypes.POINTER(KvDesc), ctypes.POINTER(RopeDesc), vp]
+    lib.photon_rope_kv_cache_write.restype = st
     lib.photon_paged_attn_partition_quantum.argtypes = [ctypes.POINTER(DecodeDesc)]
     lib.photon_paged_attn_partition_quantum.restype = i32
     lib.photon_paged_attn_partition_tokens.argtypes = [ctypes.POINTER(DecodeDesc)]
@@ -157,6 +165,44 @@ def kv_cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
     check(lib.photon_kv_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
                                     slot_mapping.shape[0], k_cache.data_ptr(), v_cache.data_ptr(),
                                     ctypes.byref(desc), _stream_ptr(k_cache)))
+
+
+def rope_kv_cache_write(q, k, v, positions, slot_mapping, k_cache, v_cache, base: float,
+                        adjacent_pairs: bool = False, q_out=None):
+    """Rotate q and k by their tokens' positions, then write rotated k and v to their slots.
+
+    q: [T, Hq, D]; k, v: [T, Hkv, D]; positions, slot_mapping: [T] int32;
+    pools [NB, Hkv, 16, D] are updated in place.  Returns q_out (a new
+    tensor unless given; passing q itself rotates q in place).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("positions", positions),
+                    ("slot_mapping", slot_mapping), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _contig(name, t)
+    if any(t.dtype != k_cache.dtype for t in (q, k, v, v_cache)):
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q, k, v and pools differ in dtype")
+    if positions.dtype != torch.int32 or slot_mapping.dtype != torch.int32:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          "positions and slot_mapping must be int32")
+    t_, hq, d = q.shape
+    _, hkv, _, d2 = k_cache.shape
+    if d != d2 or tuple(k.shape) != (t_, hkv, d) or v.shape != k.shape \
+            or tuple(positions.shape) != (t_,) or tuple(slot_mapping.shape) != (t_,) \
+            or v_cache.shape != k_cache.shape:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    else:
+        _contig("q_out", q_out)
+        if q_out.shape != q.shape or q_out.dtype != q.dtype:
+            raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q_out shape or dtype")
+    desc = kv_desc(k_cache)
+    rope = RopeDesc(float(base), int(bool(adjacent_pairs)), 0)
+    check(lib.photon_rope_kv_cache_write(q.data_ptr(), q_out.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         positions.data_ptr(), slot_mapping.data_ptr(), t_, hq,
+                                         k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(desc),
+                                         ctypes.byref(rope), _stream_ptr(k_cache)))
+    return q_out
 
 
 def partition_quantum(desc: DecodeDesc) -> int:

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libphoton_decode.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["photon_abi.hip", "kv_cache_write.hip", "paged_decode.hip"]
+SOURCES = ["photon_abi.hip", "kv_cache_write.hip", "paged_decode.hip", "rope_kv_write.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

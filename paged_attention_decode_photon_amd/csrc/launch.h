@@ -78,6 +78,28 @@ struct DecodeArgs {
 // One decode launch on stream (partitions merge inside the same kernel).
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
 
+struct RopeArgs {
+    const void *q;
+    void *q_out;  // may equal q
+    const void *k;
+    const void *v;
+    const int32_t *positions;
+    const int32_t *slot_mapping;
+    void *k_cache;
+    void *v_cache;
+    double base;
+    int num_tokens;
+    int num_q_heads;
+    int num_kv_heads;
+    int head_dim;
+    int block_size;
+    int dtype;
+    int adjacent_pairs;  // 1: pairs (2j, 2j+1); 0: pairs (j, j + D/2)
+};
+
+// Rotary embedding of q and k, then the slot-mapped write of rotated k and v.
+hipError_t launch_rope_kv_cache_write(const RopeArgs &a, hipStream_t stream);
+
 hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slots,
                                  int num_tokens, void *k_cache, void *v_cache, int num_kv_heads,
                                  int block_size, int row_bytes, hipStream_t stream);

@@ -63,117 +63,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "elem.h"
 #include "lane_ops.h"
 #include "launch.h"
 
 namespace photon {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
-
 // Fourth descriptor word of a raw (unswizzled, stride 0) buffer on gfx9-family.
 constexpr int kRawBufferWord3 = 0x00020000;
 
-
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
-
-template <typename T>
-struct Elem;
-
-template <>
-struct Elem<float> {
-    __device__ static void unpack(const u32x4 &v, float (&f)[4])
-    {
-        f[0] = __uint_as_float(v[0]);
-        f[1] = __uint_as_float(v[1]);
-        f[2] = __uint_as_float(v[2]);
-        f[3] = __uint_as_float(v[3]);
-    }
-    __device__ static u32x4 pack(const float (&f)[4])
-    {
-        return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                     __float_as_uint(f[3])};
-    }
-    __device__ static float from_float(float x) { return x; }
-};
-
-template <>
-struct Elem<_Float16> {
-    __device__ static void unpack(const u32x4 &v, float (&f)[8])
-    {
-        // Copy each dword out of the vector before the bit cast: a bit cast of
-        // the vector element itself reads the vector's first dword.
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t word = v[i];
-            half2_t h = __builtin_bit_cast(half2_t, word);
-            f[2 * i] = (float)h[0];
-            f[2 * i + 1] = (float)h[1];
-        }
-    }
-    __device__ static u32x4 pack(const float (&f)[8])
-    {
-        u32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            half2_t h;
-            h[0] = (_Float16)f[2 * i];
-            h[1] = (_Float16)f[2 * i + 1];
-            const uint32_t word = __builtin_bit_cast(uint32_t, h);
-            v[i] = word;
-        }
-        return v;
-    }
-    __device__ static _Float16 from_float(float x) { return (_Float16)x; }
-};
-
-// bfloat16 is the upper half of a binary32, so widening is a shift; narrowing
-// rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
-template <>
-struct Elem<__bf16> {
-    __device__ static void unpack(const u32x4 &v, float (&f)[8])
-    {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t word = v[i];
-            f[2 * i] = __uint_as_float(word << 16);
-            f[2 * i + 1] = __uint_as_float(word & 0xffff0000u);
-        }
-    }
-    __device__ static u32x4 pack(const float (&f)[8])
-    {
-        u32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bf162_t h;
-            h[0] = (__bf16)f[2 * i];
-            h[1] = (__bf16)f[2 * i + 1];
-            const uint32_t word = __builtin_bit_cast(uint32_t, h);
-            v[i] = word;
-        }
-        return v;
-    }
-    __device__ static __bf16 from_float(float x) { return (__bf16)x; }
-};
-
-// Store E consecutive outputs of type O (E * sizeof(O) is 16 or 32 bytes).
-template <typename O, int E>
-__device__ __forceinline__ void store_out(O *dst, const float (&v)[E])
-{
-    if constexpr (sizeof(O) == 4) {
-#pragma unroll
-        for (int k = 0; k < E / 4; ++k)
-            *reinterpret_cast<u32x4 *>(dst + 4 * k) =
-                u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
-                      __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
-    } else {
-        static_assert(E * sizeof(O) == 16, "one 16-byte store");
-        *reinterpret_cast<u32x4 *>(dst) = Elem<O>::pack(v);
-    }
-}
 
 template <typename T, int D, int G>
 struct Shape {

@@ -197,6 +197,60 @@ photon_status photon_kv_cache_write(const void *k, const void *v, const int32_t 
     return ok();
 }
 
+photon_status photon_rope_kv_cache_write(const void *q, void *q_out, const void *k, const void *v,
+                                         const int32_t *positions, const int32_t *slot_mapping,
+                                         int32_t num_tokens, int32_t num_q_heads, void *k_cache,
+                                         void *v_cache, const photon_kv_desc *kv,
+                                         const photon_rope_desc *rope, void *stream)
+{
+    photon_status st = check_kv(kv);
+    if (st != PHOTON_OK)
+        return st;
+    if (!rope)
+        return fail(PHOTON_ERR_INVALID_ARG, "rope descriptor is NULL");
+    if (!std::isfinite(rope->base) || !(rope->base > 0.0))
+        return fail(PHOTON_ERR_INVALID_ARG, "rope base %g must be finite and positive", rope->base);
+    if ((rope->adjacent_pairs != 0 && rope->adjacent_pairs != 1) || rope->reserved != 0)
+        return fail(PHOTON_ERR_INVALID_ARG, "rope adjacent_pairs must be 0 or 1, reserved 0");
+    if (num_tokens < 0 || num_q_heads <= 0)
+        return fail(PHOTON_ERR_INVALID_ARG, "num_tokens %d must be >= 0, num_q_heads %d > 0",
+                    num_tokens, num_q_heads);
+    if (num_tokens == 0)
+        return ok();
+    if (!q || !q_out || !k || !v || !positions || !slot_mapping || !k_cache || !v_cache)
+        return fail(PHOTON_ERR_INVALID_ARG, "NULL data pointer");
+    if (!aligned16(q) || !aligned16(q_out) || !aligned16(k) || !aligned16(v) ||
+        !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PHOTON_ERR_INVALID_ARG, "q, q_out, k, v and the pools must be 16-byte aligned");
+    if (!aligned4(positions) || !aligned4(slot_mapping))
+        return fail(PHOTON_ERR_INVALID_ARG, "positions and slot_mapping must be 4-byte aligned");
+    const size_t q_bytes = (size_t)num_tokens * num_q_heads * kv->head_dim * elem_bytes_of(kv->dtype);
+    const char *qb = static_cast<const char *>(q), *ob = static_cast<const char *>(q_out);
+    if (qb != ob && qb < ob + q_bytes && ob < qb + q_bytes)
+        return fail(PHOTON_ERR_INVALID_ARG, "q_out overlaps q without being equal to it");
+    photon::RopeArgs a{};
+    a.q = q;
+    a.q_out = q_out;
+    a.k = k;
+    a.v = v;
+    a.positions = positions;
+    a.slot_mapping = slot_mapping;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.base = rope->base;
+    a.num_tokens = num_tokens;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = kv->num_kv_heads;
+    a.head_dim = kv->head_dim;
+    a.block_size = kv->block_size;
+    a.dtype = kv->dtype;
+    a.adjacent_pairs = rope->adjacent_pairs;
+    hipError_t err = photon::launch_rope_kv_cache_write(a, (hipStream_t)stream);
+    if (err != hipSuccess)
+        return fail(PHOTON_ERR_HIP, "rope cache write launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
 int32_t photon_paged_attn_partition_quantum(const photon_decode_desc *desc)
 {
     Plan p;

@@ -60,9 +60,11 @@ def test_binding_structs_match_the_header(tmp_path):
     prog.write_text(
         '#include <stddef.h>\n#include <stdio.h>\n#include "photon_decode.h"\n'
         "int main(void) {\n"
-        '  printf("%zu %zu %zu %zu %zu %d %d\\n", sizeof(photon_kv_desc), sizeof(photon_decode_desc),\n'
-        "         offsetof(photon_decode_desc, kv), offsetof(photon_decode_desc, flags),\n"
-        "         offsetof(photon_kv_desc, dtype), PHOTON_BF16, PHOTON_DECODE_OUT_F32);\n"
+        '  printf("%zu %zu %zu %zu %zu %d %d %zu %zu\\n", sizeof(photon_kv_desc),\n'
+        "         sizeof(photon_decode_desc), offsetof(photon_decode_desc, kv),\n"
+        "         offsetof(photon_decode_desc, flags), offsetof(photon_kv_desc, dtype), PHOTON_BF16,\n"
+        "         PHOTON_DECODE_OUT_F32, sizeof(photon_rope_desc),\n"
+        "         offsetof(photon_rope_desc, adjacent_pairs));\n"
         "  return 0;\n}\n")
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), "-o", str(exe),
@@ -70,7 +72,8 @@ def test_binding_structs_match_the_header(tmp_path):
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     assert got == [ctypes.sizeof(pa.KvDesc), ctypes.sizeof(pa.DecodeDesc),
                    pa.DecodeDesc.kv.offset, pa.DecodeDesc.flags.offset, pa.KvDesc.dtype.offset,
-                   pa.BF16, pa.DECODE_OUT_F32]
+                   pa.BF16, pa.DECODE_OUT_F32, ctypes.sizeof(pa.RopeDesc),
+                   pa.RopeDesc.adjacent_pairs.offset]
 
 
 def write(desc, n=4, k=FAKE, v=FAKE, slots=FAKE, kc=FAKE, vc=FAKE):
@@ -184,3 +187,41 @@ def test_decode_rejects_bad_pointers_scale_and_workspace():
 def test_decode_with_no_sequences_launches_nothing():
     assert _decode(dd(b=0), q=None, kc=None, vc=None, tables=None, lens=None, out=None,
                    ws=None, ws_bytes=0) == pa.OK
+
+
+def _rope(kvd=None, rope=None, n=4, hq=32, q=FAKE, q_out=FAKE + 0x100000, k=FAKE, v=FAKE,
+          pos=FAKE, slots=FAKE, kc=FAKE, vc=FAKE):
+    kvd = kv() if kvd is None else kvd
+    rope = pa.RopeDesc(1e4, 0, 0) if rope is None else rope
+    return pa.lib.photon_rope_kv_cache_write(q, q_out, k, v, pos, slots, n, hq, kc, vc,
+                                             ctypes.byref(kvd),
+                                             ctypes.byref(rope) if rope is not False else None,
+                                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rope=False), pa.ERR_INVALID_ARG),
+    (dict(rope=pa.RopeDesc(0.0, 0, 0)), pa.ERR_INVALID_ARG),
+    (dict(rope=pa.RopeDesc(-1e4, 0, 0)), pa.ERR_INVALID_ARG),
+    (dict(rope=pa.RopeDesc(float("nan"), 0, 0)), pa.ERR_INVALID_ARG),
+    (dict(rope=pa.RopeDesc(float("inf"), 0, 0)), pa.ERR_INVALID_ARG),
+    (dict(rope=pa.RopeDesc(1e4, 2, 0)), pa.ERR_INVALID_ARG),
+    (dict(rope=pa.RopeDesc(1e4, 0, 1)), pa.ERR_INVALID_ARG),
+    (dict(kvd=kv(d=96)), pa.ERR_UNSUPPORTED),
+    (dict(kvd=kv(dtype=5)), pa.ERR_INVALID_ARG),
+    (dict(hq=0), pa.ERR_INVALID_ARG),
+    (dict(n=-1), pa.ERR_INVALID_ARG),
+    (dict(q=None), pa.ERR_INVALID_ARG),
+    (dict(pos=None), pa.ERR_INVALID_ARG),
+    (dict(q_out=FAKE + 8), pa.ERR_INVALID_ARG),      # misaligned
+    (dict(pos=FAKE + 2), pa.ERR_INVALID_ARG),
+    (dict(q_out=FAKE + 16), pa.ERR_INVALID_ARG),     # overlaps q without being q
+])
+def test_rope_cache_write_rejects_bad_arguments(kw, code):
+    assert _rope(**kw) == code
+    assert detail()
+
+
+def test_rope_cache_write_with_no_tokens_launches_nothing():
+    assert _rope(n=0, q=None, q_out=None, k=None, v=None, pos=None, slots=None, kc=None,
+                 vc=None) == pa.OK
