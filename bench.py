@@ -223,6 +223,45 @@ def rope_measurements(args, cfg, lay, layers, slots, device, stream):
     }
 
 
+def scheduler_measurements(trace_name: str = "serving"):
+    """Host cost of the native block manager + scheduler over a seeded request
+    trace (every step: admit arrivals, schedule, update), next to the plain
+    Python reference scheduler on the same trace."""
+    from paged_attention_decode_photon_amd.sched import Scheduler
+    from oracle.scheduler import OracleScheduler
+
+    tc = di.TRACES[trace_name]
+    trace = di.make_request_trace(tc)
+
+    def drive(s):
+        per_step, i, done, tokens = [], 0, 0, 0
+        step = 0
+        while done < len(trace):
+            t0 = time.perf_counter()
+            while i < len(trace) and trace[i][0] <= step:
+                s.add_request(*trace[i][1:])
+                i += 1
+            out = s.schedule()
+            done += len(s.update())
+            per_step.append(time.perf_counter() - t0)
+            tokens += len(out["slot_mapping"])
+            step += 1
+        return per_step, tokens
+
+    nat, tokens = drive(Scheduler(**tc.sched_config()))
+    ref, _ = drive(OracleScheduler(**tc.sched_config()))
+    return {
+        "trace": trace_name,
+        "requests": len(trace),
+        "steps": len(nat),
+        "tokens_scheduled": tokens,
+        "native_us_per_step_mean": round(1e6 * statistics.fmean(nat), 2),
+        "native_us_per_step_p99": round(1e6 * float(np.percentile(nat, 99)), 2),
+        "reference_us_per_step_mean": round(1e6 * statistics.fmean(ref), 2),
+        "note": "host time per step, Python binding included; max_seqs 64, 2048-token budget",
+    }
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -432,6 +471,7 @@ def main(argv=None) -> int:
     }
     if rope is not None:
         result["rope_kv_cache_write"] = rope
+    result["scheduler"] = scheduler_measurements()
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, lay, host_layers, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -287,3 +287,61 @@ def poison_unused(cfg: DecodeConfig, layout: BatchLayout, pool: np.ndarray) -> n
             bits[last, :, c % bs:, :] = nan
     bits[~used] = nan
     return out
+
+
+# ----------------------------------------------------------- request traces
+
+@dataclasses.dataclass(frozen=True)
+class TraceConfig:
+    """A seeded stream of requests for the continuous-batching scheduler.
+
+    Arrivals: exponential gaps of mean ``mean_gap`` steps (rounded down, so
+    several requests may arrive at one step); prompt lengths log-uniform in
+    [prompt_lo, prompt_hi]; generated lengths uniform in [new_lo, new_hi].
+    The pool and step limits are the scheduler's configuration.
+    """
+
+    name: str
+    seed: int
+    num_requests: int
+    mean_gap: float
+    prompt_lo: int
+    prompt_hi: int
+    new_lo: int
+    new_hi: int
+    num_blocks: int
+    max_seqs: int
+    max_tokens_per_step: int
+    max_blocks_per_seq: int
+    block_size: int = BLOCK_SIZE
+
+    def sched_config(self) -> dict:
+        return dict(num_blocks=self.num_blocks, block_size=self.block_size,
+                    max_seqs=self.max_seqs, max_tokens_per_step=self.max_tokens_per_step,
+                    max_blocks_per_seq=self.max_blocks_per_seq)
+
+
+TRACES: dict[str, TraceConfig] = {
+    # Small and tight: the pool holds a few requests, so preemption is frequent.
+    "tight": TraceConfig("tight", 10, 40, 0.7, 4, 120, 1, 40, num_blocks=24, max_seqs=6,
+                         max_tokens_per_step=64, max_blocks_per_seq=12),
+    # Larger pool, long prompts chunked by the token budget.
+    "chunked": TraceConfig("chunked", 11, 120, 0.3, 16, 2048, 8, 128, num_blocks=600,
+                           max_seqs=32, max_tokens_per_step=512, max_blocks_per_seq=136),
+    # Llama-3.2-1B-like serving: batch up to 64, 2048-token budget, 4096 blocks.
+    "serving": TraceConfig("serving", 12, 256, 0.25, 16, 2048, 16, 256, num_blocks=4096,
+                           max_seqs=64, max_tokens_per_step=2048, max_blocks_per_seq=144),
+}
+
+
+def make_request_trace(tc: TraceConfig) -> list[tuple[int, int, int, int]]:
+    """[(arrival_step, request_id, prompt_len, max_new_tokens)] sorted by arrival."""
+    rng = np.random.default_rng(tc.seed)
+    gaps = rng.exponential(tc.mean_gap, tc.num_requests)
+    arrival = np.floor(np.cumsum(gaps)).astype(np.int64)
+    u = rng.uniform(math.log(tc.prompt_lo), math.log(tc.prompt_hi + 1), tc.num_requests)
+    prompt = np.clip(np.floor(np.exp(u)), tc.prompt_lo, tc.prompt_hi).astype(np.int64)
+    new = rng.integers(tc.new_lo, tc.new_hi, tc.num_requests, endpoint=True)
+    cap = min(tc.max_blocks_per_seq, tc.num_blocks) * tc.block_size
+    new = np.minimum(new, cap + 1 - prompt)  # the longest a request may grow
+    return [(int(a), i, int(p), int(n)) for i, (a, p, n) in enumerate(zip(arrival, prompt, new))]

@@ -23,9 +23,12 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libphoton_decode.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["photon_abi.hip", "kv_cache_write.hip", "paged_decode.hip", "rope_kv_write.hip"]
+HOST_SOURCES = ["scheduler.cpp"]  # host-only C++ (the block manager and scheduler)
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-fvisibility=hidden"]
 COMMON = [
     f"--offload-arch={ARCH}", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -35,10 +38,13 @@ COMMON = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src in HOST_SOURCES:
+        cmd = [CXX, *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        raise RuntimeError(f"{cmd[0]} failed for {src}:\n{r.stderr}")
     # the host pass does not know the device-only feature; drop that line
     noise = "is not a recognized feature for this target"
     rest = [ln for ln in r.stderr.splitlines() if noise not in ln and ln.strip()]
@@ -48,11 +54,12 @@ def _compile(src: str) -> str:
 
 
 def build(jobs: int | None = None) -> str:
-    """Compile every HIP source for gfx950 and link the shared library; returns its path."""
+    """Compile every HIP source for gfx950 (and the host C++ sources), link the shared library."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    sources = SOURCES + HOST_SOURCES
+    jobs = jobs or min(len(sources), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, sources))
     tmp = LIB + f".tmp{os.getpid()}"
     subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

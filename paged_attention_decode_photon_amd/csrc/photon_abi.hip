@@ -14,10 +14,13 @@
 
 #include "launch.h"
 #include "photon_decode.h"
+#include "status.h"
+
+namespace photon {
 
 namespace {
-
 thread_local char g_detail[256] = "";
+}  // namespace
 
 photon_status fail(photon_status st, const char *fmt, ...)
 {
@@ -33,6 +36,15 @@ photon_status ok()
     g_detail[0] = '\0';
     return PHOTON_OK;
 }
+
+const char *last_detail() { return g_detail; }
+
+}  // namespace photon
+
+namespace {
+
+using photon::fail;
+using photon::ok;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -338,7 +350,7 @@ const char *photon_status_str(photon_status status)
     return "PHOTON_UNKNOWN_STATUS";
 }
 
-const char *photon_last_error_detail(void) { return g_detail; }
+const char *photon_last_error_detail(void) { return photon::last_detail(); }
 
 int32_t photon_abi_version(void) { return PHOTON_ABI_VERSION; }
 

@@ -12,20 +12,24 @@ import pytest
 
 import paged_attention_decode_photon_amd as pa
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                      "include", "photon_decode.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "photon_decode.h")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 FAKE = 0x10000  # aligned, never dereferenced: each call below fails validation first
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return re.findall(r"PHOTON_API\s+[\w\s\*]+?\b(photon_\w+)\s*\(", text)
+    names = []
+    for h in HEADERS:
+        names += re.findall(r"PHOTON_API\s+[\w\s\*]+?\b(photon_\w+)\s*\(", open(h).read())
+    return names
 
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"photon_kv_cache_write", "photon_paged_attn_decode",
-            "photon_paged_attn_workspace_bytes", "photon_status_str"} <= names
+    assert {"photon_kv_cache_write", "photon_paged_attn_decode", "photon_rope_kv_cache_write",
+            "photon_paged_attn_workspace_bytes", "photon_status_str", "photon_sched_create",
+            "photon_sched_schedule", "photon_sched_update"} <= names
 
 
 @pytest.mark.parametrize("name", declared_functions())
@@ -225,3 +229,21 @@ def test_rope_cache_write_rejects_bad_arguments(kw, code):
 def test_rope_cache_write_with_no_tokens_launches_nothing():
     assert _rope(n=0, q=None, q_out=None, k=None, v=None, pos=None, slots=None, kc=None,
                  vc=None) == pa.OK
+
+
+def test_scheduler_structs_match_the_header(tmp_path):
+    from paged_attention_decode_photon_amd import sched
+    prog = tmp_path / "sched_layout.c"
+    prog.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "photon_sched.h"\n'
+        "int main(void) {\n"
+        '  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(photon_sched_config), sizeof(photon_sched_batch),\n'
+        "         offsetof(photon_sched_batch, request_ids), offsetof(photon_sched_batch, preempted_ids),\n"
+        "         sizeof(photon_sched_request_info), offsetof(photon_sched_request_info, num_preemptions));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "sched_layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", INCLUDE, "-o", str(exe), str(prog)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    assert got == [ctypes.sizeof(sched.SchedConfig), ctypes.sizeof(sched.SchedBatch),
+                   sched.SchedBatch.request_ids.offset, sched.SchedBatch.preempted_ids.offset,
+                   ctypes.sizeof(sched.SchedRequestInfo), sched.SchedRequestInfo.num_preemptions.offset]
