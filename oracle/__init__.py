@@ -76,6 +76,10 @@ def _configure(lib):
                                              i64, ctypes.c_int, ctypes.c_double, vp, vp,
                                              ctypes.c_int]
     lib.oracle_paged_attn_decode.restype = ctypes.c_int
+    lib.oracle_paged_attn_multi_query.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                  i64, i64, ctypes.c_int, ctypes.c_double, vp,
+                                                  ctypes.c_int]
+    lib.oracle_paged_attn_multi_query.restype = ctypes.c_int
     lib.oracle_rope.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                 vp]
     lib.oracle_rope.restype = ctypes.c_int
@@ -231,3 +235,35 @@ def rope_kv_cache_write(q, k, v, positions, slot_mapping, k_cache, v_cache, base
         if s >= 0:
             k_new[s // bs, :, s % bs, :] = k_rot[i]
     return q_out, k_new, v_new
+
+
+def paged_attn_multi_query(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                           block_tables: np.ndarray, context_lens: np.ndarray,
+                           query_start: np.ndarray, scale: float, num_threads: int = 0) -> np.ndarray:
+    """fp64 multi-query attention with a causal tail; returns out [T, Hq, D].
+
+    Sequence b owns q rows query_start[b] .. query_start[b+1]-1, the last
+    n_b of its context_lens[b] tokens; row j attends to positions
+    <= context_lens[b] - n_b + j.
+    """
+    q = np.ascontiguousarray(q)
+    kc = np.ascontiguousarray(k_cache)
+    vc = np.ascontiguousarray(v_cache)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    if q.dtype not in _DTYPE_CODE or kc.dtype != q.dtype or vc.dtype != q.dtype:
+        raise OracleError(ERR_ARG, "dtype")
+    t, hq, d = q.shape
+    nb, hkv, bs, d2 = kc.shape
+    b = len(lens)
+    if d2 != d or vc.shape != kc.shape or tables.ndim != 2 or tables.shape[0] != b \
+            or qs.shape != (b + 1,) or (b and qs[-1] != t):
+        raise OracleError(ERR_ARG, "shape mismatch")
+    out = np.full((t, hq, d), np.nan, dtype=np.float64)
+    rc = _load().oracle_paged_attn_multi_query(_ptr(q), _ptr(kc), _ptr(vc), _ptr(tables), _ptr(lens),
+                                               _ptr(qs), b, hq, hkv, d, bs, nb, tables.shape[1],
+                                               _code(q), float(scale), _ptr(out), int(num_threads))
+    if rc != OK:
+        raise OracleError(rc, "paged_attn_multi_query")
+    return out

@@ -244,6 +244,105 @@ int oracle_paged_attn_decode(const void *q, const void *k_cache, const void *v_c
     return rc;
 }
 
+/* Multi-query paged attention with a causal tail (chunked prefill and
+ * speculative verification: several new tokens of a sequence attend at
+ * once).  Sequence b owns query rows query_start[b] .. query_start[b+1]-1;
+ * with n_b = query_start[b+1] - query_start[b] and ctx = context_lens[b]
+ * (which counts the new tokens), query row j of b is the token at position
+ * p = ctx - n_b + j and attends to the cached tokens t <= p.  Each (row,
+ * query head) is the single-query step of oracle_paged_attn_decode with the
+ * context cut at p + 1: two passes in double, sums in token order.
+ *   q, out  [T, Hq, D] (out in double), T = query_start[B]
+ * Preconditions (errors, not undefined behaviour): query_start starts at 0
+ * and never decreases, n_b <= ctx_b <= max_blocks * block_size, used block
+ * ids in range. */
+int oracle_paged_attn_multi_query(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const int32_t *query_start, int64_t num_seqs,
+                                  int64_t num_q_heads, int64_t num_kv_heads, int64_t head_dim,
+                                  int64_t block_size, int64_t num_blocks, int64_t max_blocks,
+                                  int dtype, double scale, double *out, int num_threads)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_blocks <= 0 || max_blocks <= 0 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+        return ORACLE_ERR_ARG;
+    if (num_q_heads % num_kv_heads != 0)
+        return ORACLE_ERR_HEADS;
+    if (num_seqs == 0)
+        return ORACLE_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+        return ORACLE_ERR_ARG;
+    if (query_start[0] != 0)
+        return ORACLE_ERR_ARG;
+    for (int64_t b = 0; b < num_seqs; ++b) {
+        const int64_t n = (int64_t)query_start[b + 1] - query_start[b];
+        const int64_t ctx = context_lens[b];
+        if (n < 0 || ctx < n || ctx > max_blocks * block_size)
+            return ORACLE_ERR_CTX;
+        const int64_t nblk = (ctx + block_size - 1) / block_size;
+        for (int64_t i = 0; i < nblk; ++i) {
+            const int64_t id = block_tables[b * max_blocks + i];
+            if (id < 0 || id >= num_blocks)
+                return ORACLE_ERR_BLOCK_RANGE;
+        }
+    }
+    const int64_t group = num_q_heads / num_kv_heads;
+    const int64_t rows = (int64_t)query_start[num_seqs] * num_q_heads;
+    int rc = ORACLE_OK;
+#ifdef _OPENMP
+    if (num_threads <= 0)
+        num_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads)
+#else
+    (void)num_threads;
+#endif
+    for (int64_t row = 0; row < rows; ++row) {
+        const int64_t tok = row / num_q_heads; /* query row (token) index */
+        const int64_t h = row % num_q_heads;
+        const int64_t g = h / group;
+        int64_t b = 0;
+        while (query_start[b + 1] <= tok)
+            ++b;
+        const int64_t n = (int64_t)query_start[b + 1] - query_start[b];
+        const int64_t j = tok - query_start[b];
+        const int64_t p = (int64_t)context_lens[b] - n + j; /* this token's position */
+        const int64_t len = p + 1;                          /* tokens it attends to */
+        double *o = out + row * head_dim;
+        double *s = (double *)malloc(sizeof(double) * (size_t)len);
+        if (!s) {
+            rc = ORACLE_ERR_ARG;
+            continue;
+        }
+        double m = -INFINITY;
+        for (int64_t t = 0; t < len; ++t) {
+            const int64_t blk = block_tables[b * max_blocks + t / block_size];
+            const int64_t kr = ((blk * num_kv_heads + g) * block_size + t % block_size) * head_dim;
+            double dot = 0.0;
+            for (int64_t d = 0; d < head_dim; ++d)
+                dot += widen(q, row * head_dim + d, dtype) * widen(k_cache, kr + d, dtype);
+            s[t] = scale * dot;
+            if (s[t] > m)
+                m = s[t];
+        }
+        double l = 0.0;
+        for (int64_t d = 0; d < head_dim; ++d)
+            o[d] = 0.0;
+        for (int64_t t = 0; t < len; ++t) {
+            const int64_t blk = block_tables[b * max_blocks + t / block_size];
+            const int64_t vr = ((blk * num_kv_heads + g) * block_size + t % block_size) * head_dim;
+            const double e = exp(s[t] - m);
+            l += e;
+            for (int64_t d = 0; d < head_dim; ++d)
+                o[d] += e * widen(v_cache, vr + d, dtype);
+        }
+        for (int64_t d = 0; d < head_dim; ++d)
+            o[d] /= l;
+        free(s);
+    }
+    return rc;
+}
+
 /* Rotary position embedding (the README's "GPU-optimised kernels" section
  * lists batched RoPE among its fused operations; the rotation itself is the
  * textbook one of RoFormer).  Each head row x of token i is split into D/2

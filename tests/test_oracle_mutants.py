@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import tests.test_oracle_pins as pins
+import tests.test_oracle_multi_query as mq
 import tests.test_oracle_rope as rp
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "photon_oracle.c")
@@ -57,6 +58,13 @@ MUTANTS = {
                                  "const double angle = (double)(positions[i] + 1) *"),
     "rope_sin_cos_swapped": ("const double c = cos(angle), s = sin(angle);",
                              "const double c = sin(angle), s = cos(angle);"),
+    "mq_causal_limit_exclusive": ("const int64_t len = p + 1;", "const int64_t len = p;"),
+    "mq_causal_limit_open": ("const int64_t len = p + 1;", "const int64_t len = context_lens[b];"),
+    "mq_positions_from_zero": ("const int64_t p = (int64_t)context_lens[b] - n + j;",
+                               "const int64_t p = j;"),
+    "mq_sequence_lookup": ("while (query_start[b + 1] <= tok)", "while (query_start[b + 1] < tok)"),
+    "mq_query_row_uses_kv_head": ("widen(q, row * head_dim + d, dtype)",
+                                  "widen(q, (tok * num_q_heads + g) * head_dim + d, dtype)"),
     "empty_ctx_not_zeroed": ("memset(o, 0, sizeof(double) * (size_t)head_dim);\n            continue;",
                              "continue;"),
 }
@@ -76,6 +84,10 @@ def _pin_suite():
         ("write_brute_f16", pins.test_cache_write_brute_force, (np.float16,)),
         ("preconditions", pins.test_precondition_errors, ()),
         ("rope_gptj", rp.test_adjacent_pairs_match_transformers_gptj, (np.float32,)),
+        ("mq_sdpa_0", mq.test_matches_torch_sdpa_with_causal_mask, (np.float32, 0)),
+        ("mq_sdpa_1", mq.test_matches_torch_sdpa_with_causal_mask, (np.float16, 1)),
+        ("mq_prefix", mq.test_whole_prompt_rows_are_prefix_decodes, ()),
+        ("mq_decode", mq.test_one_new_token_per_sequence_is_the_decode_step, ()),
         ("rope_llama", rp.test_rotate_half_matches_transformers_llama, (64,)),
         ("rope_identities", rp.test_rotation_identities, (False,)),
     ] + [(f"sdpa_{s}", pins.test_matches_torch_sdpa_float64, (np.float32, s)) for s in range(3)]
