@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PHOTON_ABI_VERSION 3
+#define PHOTON_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define PHOTON_API __attribute__((visibility("default")))
@@ -130,6 +130,59 @@ typedef struct photon_decode_desc {
 PHOTON_API photon_status photon_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                                     int32_t num_tokens, void *k_cache, void *v_cache,
                                     const photon_kv_desc *kv, void *stream);
+
+/* Shape of one multi-query call. */
+typedef struct photon_multi_query_desc {
+    int32_t num_seqs;           /* B, >= 0 (at most 65535 / num_kv_heads)         */
+    int32_t num_tokens;         /* T = query_start[B], rows of q and out, >= 0    */
+    int32_t num_q_heads;        /* Hq, a multiple of kv.num_kv_heads; the group
+                                   Hq / Hkv must be 1, 2, 4 or 8                  */
+    int32_t max_blocks_per_seq; /* row length of block_tables, > 0                */
+    int32_t max_query_len;      /* >= every query_start[b+1] - query_start[b];
+                                   sizes the grid                                 */
+    int32_t flags;              /* PHOTON_DECODE_OUT_F32 or 0                     */
+    photon_kv_desc kv;
+} photon_multi_query_desc;
+
+/*
+ * Multi-query paged attention with a causal tail: several new tokens of each
+ * sequence attend at once (chunked prefill, and the verification step of
+ * speculative decoding on the README's roadmap), over the same block-level
+ * cache and block tables as photon_paged_attn_decode (README "GPU-optimised
+ * kernels": batched paged attention).  Sequence b owns query rows
+ * query_start[b] .. query_start[b+1] - 1, which are the last
+ * n_b = query_start[b+1] - query_start[b] of its context_lens[b] tokens
+ * (already written to the cache).  Row j of sequence b is at position
+ * p = context_lens[b] - n_b + j and, for query head h and KV head
+ * g = h / (Hq / Hkv), gets
+ *
+ *   out = sum_{t <= p} exp(s_t - max s) V_t / sum_{t <= p} exp(s_t - max s),
+ *   s_t = scale * <q_row_h, K_t>.
+ *
+ * Scores and products run on the matrix cores: fp32 storage in fp32
+ * (16x16x4 MFMA), 16-bit storage with exact products and fp32 sums (16x16x16
+ * MFMA); softmax weights are applied as a 16-bit value plus its 16-bit
+ * rounding residual, so they carry about fp32 accuracy.
+ *
+ *   q             [num_tokens, num_q_heads, head_dim]     kv.dtype, 16-byte aligned
+ *   k_cache, v_cache  pools (read only), 16-byte aligned
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32
+ *   context_lens  [num_seqs] int32, n_b <= ctx <= max_blocks_per_seq * block_size
+ *   query_start   [num_seqs + 1] int32, query_start[0] = 0, non-decreasing,
+ *                 query_start[num_seqs] = num_tokens
+ *   out           [num_tokens, num_q_heads, head_dim]     kv.dtype (fp32 with
+ *                 PHOTON_DECODE_OUT_F32), 16-byte aligned
+ *
+ * No workspace.  Device-resident indices are not range-checked (caller
+ * error).  num_seqs == 0 or num_tokens == 0 launches nothing.
+ */
+PHOTON_API photon_status photon_paged_attn_multi_query(const void *q, const void *k_cache,
+                                                       const void *v_cache,
+                                                       const int32_t *block_tables,
+                                                       const int32_t *context_lens,
+                                                       const int32_t *query_start, float scale,
+                                                       const photon_multi_query_desc *desc,
+                                                       void *out, void *stream);
 
 /* Rotary embedding parameters of photon_rope_kv_cache_write. */
 typedef struct photon_rope_desc {

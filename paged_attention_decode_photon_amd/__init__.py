@@ -58,6 +58,12 @@ class DecodeDesc(ctypes.Structure):
                 ("partition_tokens", ctypes.c_int32), ("kv", KvDesc), ("flags", ctypes.c_int32)]
 
 
+class MultiQueryDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("max_query_len", ctypes.c_int32), ("flags", ctypes.c_int32), ("kv", KvDesc)]
+
+
 class RopeDesc(ctypes.Structure):
     _fields_ = [("base", ctypes.c_double), ("adjacent_pairs", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
@@ -86,6 +92,9 @@ def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     st = ctypes.c_int
     lib.photon_kv_cache_write.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.POINTER(KvDesc), vp]
     lib.photon_kv_cache_write.restype = st
+    lib.photon_paged_attn_multi_query.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                                  ctypes.POINTER(MultiQueryDesc), vp, vp]
+    lib.photon_paged_attn_multi_query.restype = st
     lib.photon_rope_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp,
                                                ctypes.POINTER(KvDesc), ctypes.POINTER(RopeDesc), vp]
     lib.photon_rope_kv_cache_write.restype = st
@@ -284,4 +293,52 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
                                        block_tables.data_ptr(), context_lens.data_ptr(),
                                        float(scale), ctypes.byref(desc), out.data_ptr(), ws_ptr,
                                        ws_len, _stream_ptr(q)))
+    return out
+
+
+def paged_attn_multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start,
+                           scale: float, max_query_len: int | None = None, out=None,
+                           out_dtype=None):
+    """Causal multi-query paged attention (chunked prefill / speculative verification).
+
+    q, out: [T, Hq, D]; sequence b owns rows query_start[b] .. query_start[b+1]-1,
+    the last tokens of its context_lens[b]; row j attends to positions
+    <= context_lens[b] - n_b + j.  ``max_query_len`` bounds every n_b (read
+    back from the device, with a synchronisation, if None).
+    """
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("context_lens", context_lens),
+                    ("query_start", query_start)):
+        _contig(name, t)
+    if any(t.dtype != torch.int32 for t in (block_tables, context_lens, query_start)):
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "index tensors must be int32")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q and pools differ")
+    b = context_lens.shape[0]
+    if q.shape[2] != k_cache.shape[3] or block_tables.shape[0] != b \
+            or tuple(query_start.shape) != (b + 1,):
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if b else 0
+    if out is not None:
+        out_dtype = out.dtype
+    elif out_dtype is None:
+        out_dtype = q.dtype
+    if out_dtype not in (q.dtype, torch.float32):
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          f"output dtype {out_dtype} is neither {q.dtype} nor float32")
+    flags = DECODE_OUT_F32 if out_dtype == torch.float32 and q.dtype != torch.float32 else 0
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _contig("out", out)
+        if out.shape != q.shape:
+            raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape")
+    desc = MultiQueryDesc(b, q.shape[0], q.shape[1], block_tables.shape[1], int(max_query_len),
+                          flags, kv_desc(k_cache))
+    check(lib.photon_paged_attn_multi_query(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                            block_tables.data_ptr(), context_lens.data_ptr(),
+                                            query_start.data_ptr(), float(scale), ctypes.byref(desc),
+                                            out.data_ptr(), _stream_ptr(q)))
     return out

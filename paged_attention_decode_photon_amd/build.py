@@ -22,7 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libphoton_decode.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["photon_abi.hip", "kv_cache_write.hip", "paged_decode.hip", "rope_kv_write.hip"]
+SOURCES = ["photon_abi.hip", "kv_cache_write.hip", "paged_decode.hip", "rope_kv_write.hip",
+           "paged_multi_query.hip"]
 HOST_SOURCES = ["scheduler.cpp"]  # host-only C++ (the block manager and scheduler)
 ARCH = "gfx950"
 

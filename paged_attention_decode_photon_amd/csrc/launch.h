@@ -78,6 +78,28 @@ struct DecodeArgs {
 // One decode launch on stream (partitions merge inside the same kernel).
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
 
+struct MultiQueryArgs {
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    const int32_t *query_start;
+    void *out;
+    int num_seqs;
+    int num_kv_heads;
+    int group;
+    int head_dim;
+    int max_blocks;
+    int max_tiles;  // ceil(max_query_len * group / 16): grid x
+    int dtype;
+    int out_f32;
+    float qscale;   // scale * log2(e)
+};
+
+// Multi-query paged attention with a causal tail, one launch.
+hipError_t launch_paged_multi_query(const MultiQueryArgs &a, hipStream_t stream);
+
 struct RopeArgs {
     const void *q;
     void *q_out;  // may equal q

@@ -1,0 +1,365 @@
+// Multi-query paged attention with a causal tail, for gfx950 matrix cores.
+//
+// Operation (PhotonInfer README: "GPU-optimised kernels", batched paged
+// attention over the block-level KV cache; the roadmap's speculative
+// decoding and the scheduler's chunked admission both need several new
+// tokens of a sequence attended at once): sequence b owns query rows
+// query_start[b] .. query_start[b+1]-1, the last n_b of its context_lens[b]
+// tokens; row j of b, at position p = ctx - n_b + j, attends to the tokens
+// t <= p of its sequence through the block table:
+//   out = sum_{t<=p} exp(s_t - m) V_t / sum_{t<=p} exp(s_t - m),
+//   s_t = scale * <q, K_t>, with KV head g = h / G for query head h.
+//
+// Work decomposition.  The n_b * G query rows of one (sequence, KV head)
+// are ordered token-major (row = j * G + head offset) and cut into tiles of
+// 16 rows; a workgroup of four waves takes one tile, each wave taking every
+// fourth 16-token KV block of the tile's causal range, and the four partial
+// softmax states are merged through LDS at the end.
+//
+// Matrix-core mapping (16x16 MFMA, K = 16 for 16-bit storage, K = 4 for
+// fp32).  Per KV block the wave forms S^T = K Q^T (16 tokens x 16 rows):
+// lane l supplies token l % 16 of K and row l % 16 of Q, both over the same
+// quarter D/4 * (l / 16) .. of the head dimension, since a contraction may
+// visit the head dimension in any order as long as both operands agree;
+// each lane then holds S^T[4 (l/16) + i][l % 16], i.e. four tokens of its
+// own row, which is exactly the B-operand layout of O^T = V^T P^T.  V is
+// transposed through a per-wave LDS tile so that each lane reads four
+// consecutive tokens of one column.  For 16-bit storage P is split into a
+// rounded part and its rounding residual (two MFMAs), which keeps the
+// weights as accurate as fp32.  Masked tokens (past a row's position, or
+// past the context in the last block) get -inf scores and zero K/V rows
+// (raw buffer loads past the valid rows return zero), so pool padding never
+// reaches the arithmetic.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "elem.h"
+#include "lane_ops.h"
+#include "launch.h"
+
+namespace photon {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMqWaves = 4;
+constexpr int kRawWord3 = 0x00020000;
+constexpr int kTile = 16;  // query rows per tile, tokens per KV block
+
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Round four fp32 values to the 16-bit storage type (nearest even), as raw bits.
+template <typename T>
+__device__ __forceinline__ u32x2 round4(const float (&p)[4])
+{
+    u32x2 r;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        typedef T t2 __attribute__((ext_vector_type(2)));
+        t2 v;
+        v[0] = (T)p[2 * k];
+        v[1] = (T)p[2 * k + 1];
+        const uint32_t w = __builtin_bit_cast(uint32_t, v);
+        r[k] = w;
+    }
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void widen4(const u32x2 &w, float (&f)[4])
+{
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        typedef T t2 __attribute__((ext_vector_type(2)));
+        const uint32_t word = w[k];
+        const t2 v = __builtin_bit_cast(t2, word);
+        f[2 * k] = (float)v[0];
+        f[2 * k + 1] = (float)v[1];
+    }
+}
+
+// One 16x16x16 MFMA on raw 16-bit operands (four values per lane).
+template <typename T>
+__device__ __forceinline__ f32x4 mfma16(const u32x2 &a, const u32x2 &b, f32x4 c)
+{
+    if constexpr (sizeof(T) == 2 && __is_same(T, _Float16))
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                         __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+template <typename T, typename O, int D, int G>
+__global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs a)
+{
+    constexpr int EB = sizeof(T);
+    constexpr int QD = D / 4;              // head-dimension elements per lane
+    constexpr int NL = QD * EB / 16;       // 16-byte loads per lane per K (or V) row part
+    constexpr int NW = QD * EB / 4;        // dwords per lane per row part
+    constexpr int MT = D / 16;             // 16-wide output column tiles
+    constexpr int VS = kTile + 4;          // LDS row stride of a transposed V tile (elements)
+    constexpr int VT_BYTES = D * VS * EB;  // one wave's transposed V tile
+    constexpr int OB_BYTES = kTile * D * 4;
+    constexpr int SMEM = (kMqWaves * VT_BYTES > kMqWaves * OB_BYTES) ? kMqWaves * VT_BYTES
+                                                                     : kMqWaves * OB_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ float stat_m[kMqWaves][kTile], stat_l[kMqWaves][kTile];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gq = lane >> 4;   // lane group: head-dimension quarter, token quad
+    const int lr = lane & 15;   // this lane's row (Q, S^T column) and K token
+    const int hkv = a.num_kv_heads;
+    const int b = blockIdx.y / hkv;
+    const int g = blockIdx.y - b * hkv;
+    const int tile = blockIdx.x;
+    const int q0 = a.query_start[b];
+    const int nq = a.query_start[b + 1] - q0;
+    const int rows = nq * G;
+    if (tile * kTile >= rows)
+        return;  // the whole workgroup leaves together
+    const int ctx = a.context_lens[b];
+    const int first_pos = ctx - nq;
+    const int last_row = min(tile * kTile + kTile - 1, rows - 1);
+    const int scan_end = first_pos + last_row / G + 1;  // tokens [0, scan_end)
+    const int nblk = (scan_end + kTile - 1) / kTile;
+
+    const int r = tile * kTile + lr;  // this lane's row
+    const bool row_ok = r < rows;
+    const int rj = r / G, rh = r - (r / G) * G;
+    const int my_pos = first_pos + rj;
+    const int hq = hkv * G;
+
+    // Q operand: row r over head-dimension quarter gq (zero for padding rows,
+    // which read the tile's last real row instead of past the query rows).
+    uint32_t qw[NW];
+    {
+        const int cr = row_ok ? r : rows - 1;
+        const int cj = cr / G, ch = cr - (cr / G) * G;
+        const T *qrow = (const T *)a.q + ((size_t)(q0 + cj) * hq + (size_t)g * G + ch) * D + gq * QD;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            u32x4 v = reinterpret_cast<const u32x4 *>(qrow)[i];
+            if (!row_ok)
+                v = u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                qw[4 * i + k] = v[k];
+        }
+    }
+
+    float m_run = -INFINITY, l_lane = 0.0f;
+    f32x4 o_acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        o_acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    T *vt = reinterpret_cast<T *>(smem + wave * VT_BYTES);
+    const size_t tile_elems = (size_t)kTile * D;
+
+    for (int n = wave; n < nblk; n += kMqWaves) {
+        const int blk = __builtin_amdgcn_readfirstlane(a.block_tables[(size_t)b * a.max_blocks + n]);
+        const int valid = min(kTile, scan_end - n * kTile);
+        const size_t base = ((size_t)blk * hkv + g) * tile_elems;
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const T *)a.k_cache + base), (short)0, valid * D * EB, kRawWord3);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const T *)a.v_cache + base), (short)0, valid * D * EB, kRawWord3);
+        const int off = (lr * D + gq * QD) * EB;
+        uint32_t kw[NW], vw[NW];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const u32x4 kv = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16 * i, 0, 0);
+            const u32x4 vv = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16 * i, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                kw[4 * i + k] = kv[k];
+                vw[4 * i + k] = vv[k];
+            }
+        }
+
+        // S^T = K Q^T for this block.
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (EB == 4) {
+#pragma unroll
+            for (int k = 0; k < QD; ++k)
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[k]), __uint_as_float(qw[k]),
+                                                         s, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int k = 0; k < QD / 4; ++k)
+                s = mfma16<T>(u32x2{kw[2 * k], kw[2 * k + 1]}, u32x2{qw[2 * k], qw[2 * k + 1]}, s);
+        }
+
+        // V^T into LDS: element (d, token lr) of this lane's quarter.
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            if constexpr (EB == 4) {
+                vt[(gq * QD + w) * VS + lr] = __builtin_bit_cast(T, vw[w]);
+            } else {
+                typedef T t2 __attribute__((ext_vector_type(2)));
+                const uint32_t word = vw[w];
+                const t2 pair = __builtin_bit_cast(t2, word);
+                vt[(gq * QD + 2 * w) * VS + lr] = pair[0];
+                vt[(gq * QD + 2 * w + 1) * VS + lr] = pair[1];
+            }
+        }
+
+        // Scores in log2 units; tokens past this row's position are masked.
+        float p[4];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = n * kTile + 4 * gq + i;
+            p[i] = (row_ok && t <= my_pos) ? s[i] * a.qscale : -INFINITY;
+            bmax = fmaxf(bmax, p[i]);
+        }
+        bmax = allreduce_pair<16, OpMax>(bmax);
+        bmax = allreduce_pair<32, OpMax>(bmax);
+        const float m_new = fmaxf(m_run, bmax);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(p[i] - m_use);
+            psum += p[i];
+        }
+        l_lane = l_lane * alpha + psum;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            o_acc[t] *= alpha;
+
+        wave_sync();  // the transposed V tile is complete
+
+        // O^T += V^T P^T.
+        if constexpr (EB == 4) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const f32x4 va = *reinterpret_cast<const f32x4 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], p[i], o_acc[t], 0, 0, 0);
+            }
+        } else {
+            const u32x2 p_hi = round4<T>(p);
+            float hi[4], lo[4];
+            widen4<T>(p_hi, hi);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lo[i] = p[i] - hi[i];
+            const u32x2 p_lo = round4<T>(lo);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const u32x2 va = *reinterpret_cast<const u32x2 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
+                o_acc[t] = mfma16<T>(va, p_hi, o_acc[t]);
+                o_acc[t] = mfma16<T>(va, p_lo, o_acc[t]);
+            }
+        }
+        wave_sync();  // reads of the V tile are done before the next block overwrites it
+    }
+
+    // Merge the four waves' partial states of each row.
+    float l_row = allreduce_pair<16, OpSum>(l_lane);
+    l_row = allreduce_pair<32, OpSum>(l_row);
+    if (gq == 0) {
+        stat_m[wave][lr] = m_run;
+        stat_l[wave][lr] = l_row;
+    }
+    __syncthreads();  // also ends every wave's use of the V tiles
+    float m_all = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMqWaves; ++w)
+        m_all = fmaxf(m_all, stat_m[w][lr]);
+    float l_all = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMqWaves; ++w)
+        l_all += stat_l[w][lr] * __builtin_amdgcn_exp2f(stat_m[w][lr] - m_all);
+    // every row has token 0 in range, so m_all is finite and l_all > 0
+    const float f = __builtin_amdgcn_exp2f(m_run - m_all) / l_all;
+    float *ob = reinterpret_cast<float *>(smem) + wave * kTile * D;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ob[lr * D + 16 * t + 4 * gq + i] = o_acc[t][i] * f;
+    __syncthreads();
+
+    // Sum the four partial rows and store: thread -> (row, D/16 columns).
+    constexpr int PER = D / 16;
+    const int orow = threadIdx.x >> 4;
+    const int c0 = (threadIdx.x & 15) * PER;
+    const int rr = tile * kTile + orow;
+    if (rr < rows) {
+        const int oj = rr / G, oh = rr - (rr / G) * G;
+        float v[PER];
+        const float *o0 = reinterpret_cast<const float *>(smem);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kMqWaves; ++w)
+                acc += o0[(w * kTile + orow) * D + c0 + e];
+            v[e] = acc;
+        }
+        O *dst = (O *)a.out + ((size_t)(q0 + oj) * hq + (size_t)g * G + oh) * D + c0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            dst[e] = Elem<O>::from_float(v[e]);
+    }
+}
+
+template <typename T, typename O, int D>
+hipError_t launch_mq_group(const MultiQueryArgs &a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.num_seqs * a.num_kv_heads));
+    const dim3 block(kMqWaves * 64);
+    switch (a.group) {
+    case 1: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 8>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename O>
+hipError_t launch_mq_dim(const MultiQueryArgs &a, hipStream_t stream)
+{
+    switch (a.head_dim) {
+    case 64: return launch_mq_group<T, O, 64>(a, stream);
+    case 128: return launch_mq_group<T, O, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_mq_out(const MultiQueryArgs &a, hipStream_t stream)
+{
+    return a.out_f32 ? launch_mq_dim<T, float>(a, stream) : launch_mq_dim<T, T>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_paged_multi_query(const MultiQueryArgs &a, hipStream_t stream)
+{
+    switch (a.dtype) {
+    case kDtypeF32: return launch_mq_dim<float, float>(a, stream);
+    case kDtypeF16: return launch_mq_out<_Float16>(a, stream);
+    case kDtypeBF16: return launch_mq_out<__bf16>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace photon

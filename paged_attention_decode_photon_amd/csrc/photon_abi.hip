@@ -209,6 +209,71 @@ photon_status photon_kv_cache_write(const void *k, const void *v, const int32_t 
     return ok();
 }
 
+photon_status photon_paged_attn_multi_query(const void *q, const void *k_cache, const void *v_cache,
+                                           const int32_t *block_tables, const int32_t *context_lens,
+                                           const int32_t *query_start, float scale,
+                                           const photon_multi_query_desc *d, void *out, void *stream)
+{
+    if (!d)
+        return fail(PHOTON_ERR_INVALID_ARG, "multi-query descriptor is NULL");
+    photon_status st = check_kv(&d->kv);
+    if (st != PHOTON_OK)
+        return st;
+    if (d->num_seqs < 0 || d->num_tokens < 0 || d->num_q_heads <= 0 || d->max_blocks_per_seq <= 0 ||
+        d->max_query_len < 0)
+        return fail(PHOTON_ERR_INVALID_ARG,
+                    "bad sizes (num_seqs=%d num_tokens=%d num_q_heads=%d max_blocks_per_seq=%d "
+                    "max_query_len=%d)",
+                    d->num_seqs, d->num_tokens, d->num_q_heads, d->max_blocks_per_seq,
+                    d->max_query_len);
+    if (d->flags & ~kKnownDecodeFlags)
+        return fail(PHOTON_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)d->flags);
+    if (d->num_q_heads % d->kv.num_kv_heads != 0)
+        return fail(PHOTON_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    d->num_q_heads, d->kv.num_kv_heads);
+    const int group = d->num_q_heads / d->kv.num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return fail(PHOTON_ERR_UNSUPPORTED, "query heads per KV head %d not built (1, 2, 4, 8 are)",
+                    group);
+    if ((int64_t)d->num_seqs * d->kv.num_kv_heads > 65535)
+        return fail(PHOTON_ERR_UNSUPPORTED, "num_seqs * num_kv_heads %lld above 65535",
+                    (long long)d->num_seqs * d->kv.num_kv_heads);
+    if (d->max_query_len > d->num_tokens)
+        return fail(PHOTON_ERR_INVALID_ARG, "max_query_len %d exceeds num_tokens %d",
+                    d->max_query_len, d->num_tokens);
+    if (!std::isfinite(scale))
+        return fail(PHOTON_ERR_INVALID_ARG, "scale is not finite");
+    if (d->num_seqs == 0 || d->num_tokens == 0 || d->max_query_len == 0)
+        return ok();
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+        return fail(PHOTON_ERR_INVALID_ARG, "NULL data pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PHOTON_ERR_INVALID_ARG, "q, the pools and out must be 16-byte aligned");
+    if (!aligned4(block_tables) || !aligned4(context_lens) || !aligned4(query_start))
+        return fail(PHOTON_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
+    photon::MultiQueryArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start = query_start;
+    a.out = out;
+    a.num_seqs = d->num_seqs;
+    a.num_kv_heads = d->kv.num_kv_heads;
+    a.group = group;
+    a.head_dim = d->kv.head_dim;
+    a.max_blocks = d->max_blocks_per_seq;
+    a.max_tiles = (int)(((int64_t)d->max_query_len * group + 15) / 16);
+    a.dtype = d->kv.dtype;
+    a.out_f32 = (d->flags & PHOTON_DECODE_OUT_F32) ? 1 : 0;
+    a.qscale = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    hipError_t err = photon::launch_paged_multi_query(a, (hipStream_t)stream);
+    if (err != hipSuccess)
+        return fail(PHOTON_ERR_HIP, "multi-query launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
 photon_status photon_rope_kv_cache_write(const void *q, void *q_out, const void *k, const void *v,
                                          const int32_t *positions, const int32_t *slot_mapping,
                                          int32_t num_tokens, int32_t num_q_heads, void *k_cache,

@@ -247,3 +247,45 @@ def test_scheduler_structs_match_the_header(tmp_path):
     assert got == [ctypes.sizeof(sched.SchedConfig), ctypes.sizeof(sched.SchedBatch),
                    sched.SchedBatch.request_ids.offset, sched.SchedBatch.preempted_ids.offset,
                    ctypes.sizeof(sched.SchedRequestInfo), sched.SchedRequestInfo.num_preemptions.offset]
+
+
+def _mq(desc, q=FAKE, kc=FAKE, vc=FAKE, tables=FAKE, lens=FAKE, qs=FAKE, scale=0.125, out=FAKE):
+    return pa.lib.photon_paged_attn_multi_query(q, kc, vc, tables, lens, qs, scale,
+                                                ctypes.byref(desc) if desc is not None else None,
+                                                out, None)
+
+
+def mqd(b=4, t=16, hq=32, mb=8, mq=4, flags=0, **kw):
+    return pa.MultiQueryDesc(b, t, hq, mb, mq, flags, kv(**kw))
+
+
+@pytest.mark.parametrize("desc,code", [
+    (mqd(hq=30), pa.ERR_INVALID_ARG),
+    (mqd(hq=128), pa.ERR_UNSUPPORTED),
+    (mqd(b=-1), pa.ERR_INVALID_ARG),
+    (mqd(t=-1), pa.ERR_INVALID_ARG),
+    (mqd(mq=-1), pa.ERR_INVALID_ARG),
+    (mqd(mq=17), pa.ERR_INVALID_ARG),           # longer than all the rows
+    (mqd(mb=0), pa.ERR_INVALID_ARG),
+    (mqd(flags=4), pa.ERR_INVALID_ARG),
+    (mqd(b=9000), pa.ERR_UNSUPPORTED),          # grid y limit with 8 KV heads
+    (mqd(d=80), pa.ERR_UNSUPPORTED),
+    (mqd(dtype=9), pa.ERR_INVALID_ARG),
+])
+def test_multi_query_rejects_bad_descriptor(desc, code):
+    assert _mq(desc) == code
+    assert detail()
+
+
+def test_multi_query_rejects_bad_pointers_and_scale():
+    assert _mq(None) == pa.ERR_INVALID_ARG
+    assert _mq(mqd(), qs=None) == pa.ERR_INVALID_ARG
+    assert _mq(mqd(), out=FAKE + 8) == pa.ERR_INVALID_ARG
+    assert _mq(mqd(), qs=FAKE + 2) == pa.ERR_INVALID_ARG
+    assert _mq(mqd(), scale=float("nan")) == pa.ERR_INVALID_ARG
+
+
+def test_multi_query_with_nothing_to_do_launches_nothing():
+    assert _mq(mqd(b=0, t=0, mq=0), q=None, kc=None, vc=None, tables=None, lens=None, qs=None,
+               out=None) == pa.OK
+    assert _mq(mqd(t=0, mq=0), q=None, out=None) == pa.OK
