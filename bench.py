@@ -102,6 +102,8 @@ def parse_args(argv=None):
     ap.add_argument("--rope-prefill-tokens", type=int, default=4096,
                     help="tokens of the large fused rotary + cache-write call timed after the "
                          "step (0 skips the rotary measurements)")
+    ap.add_argument("--no-multi-query", action="store_true",
+                    help="skip the multi-query (speculative verify / chunked prefill) timings")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (default: the step is also captured in a "
                          "HIP graph and replayed, and value uses the replays)")
@@ -220,6 +222,104 @@ def rope_measurements(args, cfg, lay, layers, slots, device, stream):
         "prefill_us_per_call": round(prefill_us, 3),
         "prefill_bytes_per_call": nbytes,
         "prefill_gbps": round(nbytes / (prefill_us * 1e-6) / 1e9, 1),
+    }
+
+
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0}  # dense, MI355X
+
+
+def multi_query_measurements(args, cfg, lay, layers, device, stream):
+    """Time the multi-query (causal tail) kernel at two shapes.
+
+    Speculative verification: every sequence of the workload verifies 4
+    tokens against its whole context, one call per layer pool (HBM-bound;
+    algorithmic bytes as for decode, with 4 query rows per sequence).
+    Chunked prefill: 4 sequences computing 512-token chunks (bf16, contexts
+    2048, 512, 1500 and 4000 tokens; matrix-core-bound; algorithmic flops
+    4 * D * Hq * (p + 1) per query row at position p).
+    """
+    import paged_attention_decode_photon_amd as pa
+    import torch
+
+    def event():
+        return torch.cuda.Event(enable_timing=True)
+
+    rng = np.random.default_rng(cfg.seed + 2000)
+    n = 4
+    b = len(lay.context_lens)
+    qs = torch.arange(0, b * n + 1, n, dtype=torch.int32, device=device)
+    tables = di.to_torch(lay.block_tables).to(device)
+    lens = di.to_torch(lay.context_lens).to(device)
+    qv = [di.to_torch(di.cast(rng.standard_normal((b * n, cfg.num_q_heads, cfg.head_dim)),
+                              cfg.np_dtype)).to(device) for _ in range(2)]
+    outs = [torch.empty_like(qv[0]) for _ in range(2)]
+
+    def verify_burst():
+        for i, L in enumerate(layers):
+            pa.paged_attn_multi_query(qv[i % 2], L["kc"], L["vc"], tables, lens, qs, cfg.scale,
+                                      max_query_len=n, out=outs[i % 2])
+
+    verify_burst()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        verify_burst()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, z = event(), event()
+    a.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    z.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    verify_us = a.elapsed_time(z) * 1e3 / (args.steps * len(layers))
+    eb = cfg.elem_bytes
+    verify_bytes = (int(lay.context_lens.sum()) * cfg.num_kv_heads * cfg.head_dim * eb * 2
+                    + 2 * b * n * cfg.num_q_heads * cfg.head_dim * eb
+                    + int(di.blocks_needed(lay.context_lens).sum()) * 4 + 4 * b + 4 * (b + 1))
+
+    # chunked prefill, bf16, its own pool
+    qlens, ctx = [512, 512, 300, 512], [2048, 512, 1500, 4000]
+    hq, hkv, d = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    need = [-(-c // 16) for c in ctx]
+    nb = sum(need)
+    perm = rng.permutation(nb).astype(np.int32)
+    tab = np.full((4, max(need)), -1, np.int32)
+    p0 = 0
+    for i, k in enumerate(need):
+        tab[i, :k] = perm[p0:p0 + k]
+        p0 += k
+    qstart = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    bf = di.BF16
+    kc = di.to_torch(di.cast(rng.standard_normal((nb, hkv, 16, d)), bf)).to(device)
+    vc = di.to_torch(di.cast(rng.standard_normal((nb, hkv, 16, d)), bf)).to(device)
+    q = di.to_torch(di.cast(rng.standard_normal((int(qstart[-1]), hq, d)), bf)).to(device)
+    out = torch.empty_like(q)
+    tab_t, ctx_t = di.to_torch(tab).to(device), torch.tensor(ctx, dtype=torch.int32, device=device)
+    qs_t = di.to_torch(qstart).to(device)
+    for _ in range(2):
+        pa.paged_attn_multi_query(q, kc, vc, tab_t, ctx_t, qs_t, cfg.scale, max_query_len=512, out=out)
+    torch.cuda.synchronize()
+    reps = max(args.steps, 5)
+    a.record(stream)
+    for _ in range(reps):
+        pa.paged_attn_multi_query(q, kc, vc, tab_t, ctx_t, qs_t, cfg.scale, max_query_len=512, out=out)
+    z.record(stream)
+    torch.cuda.synchronize()
+    prefill_us = a.elapsed_time(z) * 1e3 / reps
+    flops = sum(4 * d * hq * (c - nq + j + 1) for c, nq in zip(ctx, qlens) for j in range(nq))
+    tflops = flops / (prefill_us * 1e-6) / 1e12
+    return {
+        "kernel": "paged_mq_kernel (16x16 MFMA, causal tail)",
+        "verify": {"dtype": cfg.dtype, "query_tokens_per_seq": n, "seqs": b,
+                   "us_per_call": round(verify_us, 3), "bytes_per_call": verify_bytes,
+                   "gbps": round(verify_bytes / (verify_us * 1e-6) / 1e9, 1),
+                   "frac_of_hbm_peak": round(verify_bytes / (verify_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "chunked_prefill": {"dtype": "bf16", "query_lens": qlens, "context_lens": ctx,
+                            "us_per_call": round(prefill_us, 3), "flops_per_call": flops,
+                            "tflops": round(tflops, 2),
+                            "frac_of_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS["bf16"], 4)},
     }
 
 
@@ -412,6 +512,8 @@ def main(argv=None) -> int:
 
     rope = rope_measurements(args, cfg, lay, layers, slots, device, stream) \
         if args.rope_prefill_tokens > 0 else None
+    mq = None if args.no_multi_query else \
+        multi_query_measurements(args, cfg, lay, layers, device, stream)
 
     per_decode = decode_bytes(cfg, lay.context_lens)
     n_written = int((lay.slot_mapping >= 0).sum())
@@ -471,6 +573,8 @@ def main(argv=None) -> int:
     }
     if rope is not None:
         result["rope_kv_cache_write"] = rope
+    if mq is not None:
+        result["multi_query"] = mq
     result["scheduler"] = scheduler_measurements()
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, lay, host_layers, args.cpu_seconds)
