@@ -1,22 +1,27 @@
 """Benchmark of the batched paged-attention decode step on one MI355X.
 
-One step is the whole hot path over one synthetic batch: the slot-mapped
-cache write of the batch's new tokens into every layer's pool, then the paged
-decode of every layer over the block tables (one kernel per call; split
-contexts merge inside it).  Each layer's decode follows its own write.  Inputs are generated once, copied to HBM, and stay
-resident; every layer owns its own K/V pool, so a 16-layer step touches about
-1.1 GB and the 256 MiB Infinity Cache cannot serve repeated reads.
+One step is the whole hot path over one synthetic batch: for every layer,
+the new token of each sequence is appended to that layer's block pool (the
+slot-mapped cache write, at position context_len - 1) and the layer is then
+decoded over its block tables; both happen in one launch per layer
+(photon_paged_attn_decode_step), with split contexts merged inside it.  The
+same step with a separate cache-write launch per layer is timed too, for
+comparison.  Inputs are generated once, copied to HBM, and stay resident;
+every layer owns its own K/V pool, so a 16-layer step touches about 1.1 GB
+and the 256 MiB Infinity Cache cannot serve repeated reads.
 
 Printed: one JSON line.  ``value`` is whole-step throughput in algorithmic
 GB/s (bytes the method must move: valid K/V rows, q, out, table entries and
-lengths for the decode; k/v rows and slots for the write) per measured step
-time.  ``roofline`` describes the decode kernel (one launch per decode call;
-split contexts merge inside it): its average launch time is the event-timed
-run of one step's decode launches (events recorded on the launch stream)
-divided by the number of launches.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
-the same workload.
+lengths, and the new K/V rows read and written) per measured step time
+(HIP-graph replay of the step).  ``roofline`` describes the decode kernel:
+its average launch time is the event-timed run of one step's launches
+(events recorded on the launch stream) divided by the number of launches.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload.  The fused rotary + cache-write kernel, the multi-query kernel and
+the host scheduler are timed after the step and reported in their own
+objects.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama1b_b16]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload llama1b_b16]
 """
 from __future__ import annotations
 
@@ -93,7 +98,7 @@ def rope_write_bytes(cfg: di.DecodeConfig, num_tokens: int, num_written: int) ->
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama1b_b16", choices=sorted(di.CONFIGS))
     ap.add_argument("--partition-tokens", type=int, default=0, help="0 = library's choice")
@@ -120,18 +125,26 @@ def parse_args(argv=None):
 
 
 def cpu_baseline(cfg, lay, host_layers, budget_s: float):
-    """Time the fp64 oracle on whole layers of the workload until the budget is used."""
+    """Time the fp64 oracle on whole layers of the workload until the budget is used:
+    with every host thread (the reported value), then single-threaded on a
+    fifth of the budget."""
     import oracle
     threads = oracle.max_threads()
     per_layer = decode_bytes(cfg, lay.context_lens)
-    done, t_total = 0, 0.0
-    while t_total < budget_s:
-        t = host_layers[done % len(host_layers)]
-        t0 = time.perf_counter()
-        oracle.paged_attn_decode(t.q, t.k_cache, t.v_cache, lay.block_tables, lay.context_lens,
-                                 cfg.scale, num_threads=threads)
-        t_total += time.perf_counter() - t0
-        done += 1
+
+    def timed(num_threads, budget):
+        done, t_total = 0, 0.0
+        while t_total < budget:
+            t = host_layers[done % len(host_layers)]
+            t0 = time.perf_counter()
+            oracle.paged_attn_decode(t.q, t.k_cache, t.v_cache, lay.block_tables,
+                                     lay.context_lens, cfg.scale, num_threads=num_threads)
+            t_total += time.perf_counter() - t0
+            done += 1
+        return done, t_total
+
+    done, t_total = timed(threads, budget_s)
+    done1, t1 = timed(1, budget_s / 5)
     return {
         "value": round(per_layer * done / t_total / 1e9, 4),
         "unit": "GB/s",
@@ -140,7 +153,22 @@ def cpu_baseline(cfg, lay, host_layers, budget_s: float):
         "sample": f"{done} decode calls (whole layers, all {len(lay.context_lens)} sequences) of "
                   f"the {cfg.name} workload, {t_total:.1f} s wall; cache write not included",
         "ms_per_layer": round(t_total / done * 1e3, 3),
+        "single_thread": {"value": round(per_layer * done1 / t1 / 1e9, 4), "unit": "GB/s",
+                          "cores": 1, "ms_per_layer": round(t1 / done1 * 1e3, 3),
+                          "sample": f"{done1} decode calls, {t1:.1f} s wall"},
+        "host_cpu": _host_cpu(),
     }
+
+
+def _host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def rope_measurements(args, cfg, lay, layers, slots, device, stream):
@@ -417,7 +445,20 @@ def main(argv=None) -> int:
                                               lens.data_ptr(), scale, descref, L["out"].data_ptr(),
                                               workspace.data_ptr(), ws_bytes, st))
 
+    def fused(L, st=sptr):
+        pa.check(lib.photon_paged_attn_decode_step(L["q"].data_ptr(), L["k"].data_ptr(),
+                                                   L["v"].data_ptr(), L["kc"].data_ptr(),
+                                                   L["vc"].data_ptr(), tables.data_ptr(),
+                                                   lens.data_ptr(), scale, descref,
+                                                   L["out"].data_ptr(), workspace.data_ptr(),
+                                                   ws_bytes, st))
+
     def step(st=sptr):
+        # one launch per layer: the new token's K/V append fused with decode
+        for L in layers:
+            fused(L, st)
+
+    def step_unfused(st=sptr):
         for L in layers:
             write(L, st)
         for L in layers:
@@ -452,24 +493,18 @@ def main(argv=None) -> int:
         return torch.cuda.Event(enable_timing=True)
 
     for _ in range(args.warmup):
-        for L in layers:
-            write(L)
-        for L in layers:
-            decode(L)
+        step()
     torch.cuda.synchronize()
 
-    # Timed region.  A step writes every layer's new tokens, then decodes
-    # every layer (each decode follows its own layer's write); one event pair
-    # brackets each step's run of decode launches, on the launch stream.
+    # Timed region.  A step appends every layer's new tokens and decodes
+    # every layer, one fused launch per layer; one event pair brackets each
+    # step's run of launches, on the launch stream.
     burst = [(event(), event()) for _ in range(args.steps)]
     start, stop = event(), event()
     start.record(stream)
     for i in range(args.steps):
-        for L in layers:
-            write(L)
         burst[i][0].record(stream)
-        for L in layers:
-            decode(L)
+        step()
         burst[i][1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
@@ -477,17 +512,19 @@ def main(argv=None) -> int:
     burst_us = [a.elapsed_time(b) * 1e3 / len(layers) for a, b in burst]
     call_mean = statistics.fmean(burst_us)
     call_med = statistics.median(burst_us)
+    call_p10, call_p90 = (float(x) for x in np.percentile(burst_us, [10, 90]))
 
     eager_step_ms = step_ms
     graph_step_ms = None
-    if not args.no_graph:
-        # The same step captured once in a HIP graph and replayed: one launch
-        # per step instead of 2 x layers.  The kernels issue no memsets and
-        # the workspace counters return to zero on their own, so replays are
-        # safe.
+    unfused_step_ms = None
+
+    def replay_ms(fn):
+        # fn captured once in a HIP graph and replayed.  The kernels issue no
+        # memsets and the workspace counters return to zero on their own, so
+        # replays are safe.
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step(torch.cuda.current_stream(device).cuda_stream)
+            fn(torch.cuda.current_stream(device).cuda_stream)
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
@@ -496,16 +533,21 @@ def main(argv=None) -> int:
             graph.replay()
         stop.record(stream)
         torch.cuda.synchronize()
-        graph_step_ms = start.elapsed_time(stop) / args.steps
-        step_ms = graph_step_ms
         del graph
+        return start.elapsed_time(stop) / args.steps
+
+    if not args.no_graph:
+        graph_step_ms = replay_ms(step)
+        step_ms = graph_step_ms
+        # for comparison: the same step with the separate cache-write kernel
+        unfused_step_ms = replay_ms(step_unfused)
 
     # Secondary: events around every single decode call (adds the event
     # packets' own overhead to each launch).
     single = [(event(), event()) for _ in layers]
     for (a, b), L in zip(single, layers):
         a.record(stream)
-        decode(L)
+        fused(L)
         b.record(stream)
     torch.cuda.synchronize()
     single_us = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in single)
@@ -517,10 +559,12 @@ def main(argv=None) -> int:
 
     per_decode = decode_bytes(cfg, lay.context_lens)
     n_written = int((lay.slot_mapping >= 0).sum())
-    per_write = write_bytes(cfg, T, n_written)
-    step_bytes = len(layers) * (per_decode + per_write)
+    # the fused launch also reads each new K/V row and writes it to the pool
+    per_append = 4 * n_written * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+    per_launch = per_decode + per_append
+    step_bytes = len(layers) * per_launch
     value = step_bytes / (step_ms * 1e-3) / 1e9
-    achieved = per_decode / (call_mean * 1e-6) / 1e9
+    achieved = per_launch / (call_mean * 1e-6) / 1e9
     tok_per_layer = len(lay.context_lens) / (step_ms * 1e-3 / len(layers))
 
     result = {
@@ -552,10 +596,12 @@ def main(argv=None) -> int:
         },
         "timing": "hip-graph replay of the step" if graph_step_ms else "eager launches",
         "ms_per_step_eager": round(eager_step_ms, 5),
+        "ms_per_step_unfused_write_then_decode": round(unfused_step_ms, 5) if unfused_step_ms else None,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s_per_layer": round(tok_per_layer, 1),
         "decode_call_us_mean": round(call_mean, 3),
         "decode_call_us_median": round(call_med, 3),
+        "decode_call_us_p10_p90": [round(call_p10, 3), round(call_p90, 3)],
         "decode_call_us_single_event_pair": round(single_us, 3),
         "decode_gbps_event_timed": round(achieved, 2),
         "copy_gbps_read_plus_write": round(copy_gbps, 1) if copy_gbps else None,
@@ -567,8 +613,9 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(cfg.name),
-            "kernel": "paged_decode_kernel (one launch per photon_paged_attn_decode call)",
-            "bytes_per_launch": per_decode,
+            "kernel": "paged_decode_kernel (one launch per photon_paged_attn_decode_step call: "
+                      "new-token append + decode)",
+            "bytes_per_launch": per_launch,
         },
     }
     if rope is not None:

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PHOTON_ABI_VERSION 4
+#define PHOTON_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define PHOTON_API __attribute__((visibility("default")))
@@ -287,6 +287,34 @@ PHOTON_API photon_status photon_paged_attn_decode(const void *q, const void *k_c
                                        const int32_t *block_tables, const int32_t *context_lens,
                                        float scale, const photon_decode_desc *desc, void *out,
                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step in one launch: the cache write of each sequence's new
+ * token fused with photon_paged_attn_decode (README "Technical details ->
+ * Paged attention" and "GPU-optimised kernels").  For every sequence b with
+ * ctx = context_lens[b] > 0, the rows k_new[b][h][:] and v_new[b][h][:] are
+ * stored at the sequence's position ctx - 1, i.e. pool row
+ * (block_tables[b][(ctx-1) / block_size], h, (ctx-1) % block_size), and the
+ * output is then exactly that of photon_paged_attn_decode over the ctx
+ * tokens, new one included.  This equals photon_kv_cache_write with
+ * slot_mapping[b] = block_tables[b][(ctx-1)/bs] * bs + (ctx-1) % bs followed
+ * by photon_paged_attn_decode, bit for bit.
+ *
+ *   k_new, v_new  [num_seqs, num_kv_heads, head_dim]   kv.dtype, 16-byte aligned
+ *   k_cache, v_cache  pools, updated in place
+ *   other arguments as for photon_paged_attn_decode
+ *
+ * Precondition (not checked): the block holding position ctx - 1 of a
+ * sequence is read by no other sequence of the call (it is the block being
+ * appended to).
+ */
+PHOTON_API photon_status photon_paged_attn_decode_step(const void *q, const void *k_new,
+                                                       const void *v_new, void *k_cache,
+                                                       void *v_cache, const int32_t *block_tables,
+                                                       const int32_t *context_lens, float scale,
+                                                       const photon_decode_desc *desc, void *out,
+                                                       void *workspace, size_t workspace_bytes,
+                                                       void *stream);
 
 /* Static name of a status code. */
 PHOTON_API const char *photon_status_str(photon_status status);

@@ -108,6 +108,9 @@ def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.photon_paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float,
                                              ctypes.POINTER(DecodeDesc), vp, vp, sz, vp]
     lib.photon_paged_attn_decode.restype = st
+    lib.photon_paged_attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                                  ctypes.POINTER(DecodeDesc), vp, vp, sz, vp]
+    lib.photon_paged_attn_decode_step.restype = st
     lib.photon_status_str.argtypes = [st]
     lib.photon_status_str.restype = ctypes.c_char_p
     lib.photon_last_error_detail.argtypes = []
@@ -341,4 +344,46 @@ def paged_attn_multi_query(q, k_cache, v_cache, block_tables, context_lens, quer
                                             block_tables.data_ptr(), context_lens.data_ptr(),
                                             query_start.data_ptr(), float(scale), ctypes.byref(desc),
                                             out.data_ptr(), _stream_ptr(q)))
+    return out
+
+
+def paged_attn_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                           scale: float, max_context_len: int | None = None, out=None,
+                           workspace=None, partition_tokens: int = 0):
+    """One fused decode step: store k_new[b], v_new[b] ([B, Hkv, D]) at position
+    context_lens[b] - 1 of each sequence, then attend as :func:`paged_attn_decode`."""
+    import torch
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        _contig(name, t)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          "block_tables and context_lens must be int32")
+    if any(t.dtype != k_cache.dtype for t in (q, k_new, v_new, v_cache)) or v_cache.shape != k_cache.shape:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q, new rows and pools differ")
+    b, _, d = q.shape
+    _, hkv, _, _ = k_cache.shape
+    if d != k_cache.shape[3] or tuple(k_new.shape) != (b, hkv, d) or v_new.shape != k_new.shape \
+            or block_tables.shape[0] != b or tuple(context_lens.shape) != (b,):
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if context_lens.numel() else 0
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens)
+    ws_need = workspace_bytes(desc)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _contig("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape or dtype")
+    if ws_need and workspace is None:
+        workspace = new_workspace(ws_need, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.photon_paged_attn_decode_step(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                            k_cache.data_ptr(), v_cache.data_ptr(),
+                                            block_tables.data_ptr(), context_lens.data_ptr(),
+                                            float(scale), ctypes.byref(desc), out.data_ptr(),
+                                            ws_ptr, ws_len, _stream_ptr(q)))
     return out

@@ -58,6 +58,8 @@ struct DecodeArgs {
     const void *q;
     const void *k_cache;
     const void *v_cache;
+    const void *k_new;  // fused decode step: rows appended at position ctx-1; NULL otherwise
+    const void *v_new;
     const int32_t *block_tables;
     const int32_t *context_lens;
     void *out;

@@ -142,8 +142,10 @@ __device__ __forceinline__ void reduce_scatter(float (&part)[NS])
 
 struct KernelArgs {
     const void *q;
-    const void *k_cache;
+    const void *k_cache;  // written only by the fused decode step (append_new_token)
     const void *v_cache;
+    const void *k_new;    // fused decode step: [B][Hkv][D] rows to append; NULL otherwise
+    const void *v_new;
     const int32_t *block_tables;
     const int32_t *context_lens;
     void *out;
@@ -180,6 +182,8 @@ struct WaveDecoder {
 
     // state of the current piece
     int b, g, ctx;
+    int new_pos;         // fused step: position of the appended token, else -1
+    u32x4 knew, vnew;    // fused step: this lane's column of the new K and V rows
     int nblk;      // blocks holding the sequence's context
     int win0;      // first block index of the table window
     int tbl_win;   // lane i: block_tables[b][win0 + i] (0 past the context)
@@ -240,6 +244,7 @@ struct WaveDecoder {
             for (int e = 0; e < E; ++e)
                 qf[hs][e] *= a.qscale;
         }
+        new_pos = -1;
         m_run = -INFINITY;
         l_run = 0.0f;
 #pragma unroll
@@ -377,10 +382,41 @@ struct WaveDecoder {
     {
         for (int ch = ch0; ch < ch1; ++ch) {
             cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
+            if (new_pos >= ch * CT && new_pos < (ch + 1) * CT)
+                store_new_token();
             u32x4 kd[NU], vd[NU];
             load_chunk(ch, kd, vd);
             consume_chunk(ch, kd, vd);
         }
+    }
+
+    // Fused decode step.  The segment's new K and V rows belong at position
+    // ctx - 1, inside the segment's last chunk, which only this wave reads.
+    // Each lane takes its 16-byte column of both rows from k_new / v_new when
+    // the piece starts; right before the chunk that holds the position the
+    // rows are stored to the pool and the wave waits for its stores, so that
+    // chunk's loads see them.  By then the column loads have long arrived
+    // unless that chunk is the piece's first.
+    __device__ void prepare_new_token()
+    {
+        const size_t src = ((size_t)b * a.num_kv_heads + g) * D + c * E;
+        knew = *reinterpret_cast<const u32x4 *>((const T *)a.k_new + src);
+        vnew = *reinterpret_cast<const u32x4 *>((const T *)a.v_new + src);
+        new_pos = ctx - 1;
+    }
+
+    __device__ void store_new_token() const
+    {
+        const int blk = __builtin_amdgcn_readfirstlane(
+            a.block_tables[(size_t)b * a.max_blocks + new_pos / kBlockTokens]);
+        if (r == 0) {  // lanes 0 .. L-1: one 16-byte column of the row each
+            const size_t dst =
+                (((size_t)blk * a.num_kv_heads + g) * kBlockTokens + new_pos % kBlockTokens) * D +
+                c * E;
+            *reinterpret_cast<u32x4 *>((T *)const_cast<void *>(a.k_cache) + dst) = knew;
+            *reinterpret_cast<u32x4 *>((T *)const_cast<void *>(a.v_cache) + dst) = vnew;
+        }
+        wait_vector_memory();
     }
 
     // Reduce the piece's per-lane state to per-head totals: afterwards every
@@ -617,6 +653,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         const int ch1 = piece_end - seg_begin;
 
         w.begin_piece(b, g, ctx, ch0);
+        const bool appends = a.k_new != nullptr && ch1 == nch;
+        if (appends)
+            w.prepare_new_token();
         w.run_chunks(ch0, ch1);
         w.reduce_piece();
         if (ch0 == 0 && ch1 == nch) {
@@ -653,6 +692,8 @@ hipError_t launch_typed(const DecodeArgs &d, hipStream_t stream)
     a.q = d.q;
     a.k_cache = d.k_cache;
     a.v_cache = d.v_cache;
+    a.k_new = d.k_new;
+    a.v_new = d.v_new;
     a.block_tables = d.block_tables;
     a.context_lens = d.context_lens;
     a.out = d.out;

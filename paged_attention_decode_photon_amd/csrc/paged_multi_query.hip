@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
 
     const int r = tile * kTile + lr;  // this lane's row
     const bool row_ok = r < rows;
-    const int rj = r / G, rh = r - (r / G) * G;
+    const int rj = r / G;
     const int my_pos = first_pos + rj;
     const int hq = hkv * G;
 

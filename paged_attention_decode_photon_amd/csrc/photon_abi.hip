@@ -352,10 +352,14 @@ photon_status photon_paged_attn_workspace_bytes(const photon_decode_desc *desc, 
     return ok();
 }
 
-photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
-                                       const int32_t *block_tables, const int32_t *context_lens,
-                                       float scale, const photon_decode_desc *desc, void *out,
-                                       void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+photon_status decode_impl(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                          const void *v_cache, const int32_t *block_tables,
+                          const int32_t *context_lens, float scale, const photon_decode_desc *desc,
+                          void *out, void *workspace, size_t workspace_bytes, void *stream)
 {
     Plan p;
     photon_status st = plan_decode(desc, &p);
@@ -381,6 +385,8 @@ photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const
     a.q = q;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
+    a.k_new = k_new;
+    a.v_new = v_new;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.out = out;
@@ -401,6 +407,36 @@ photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const
     if (err != hipSuccess)
         return fail(PHOTON_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                                       const int32_t *block_tables, const int32_t *context_lens,
+                                       float scale, const photon_decode_desc *desc, void *out,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale,
+                       desc, out, workspace, workspace_bytes, stream);
+}
+
+photon_status photon_paged_attn_decode_step(const void *q, const void *k_new, const void *v_new,
+                                            void *k_cache, void *v_cache,
+                                            const int32_t *block_tables,
+                                            const int32_t *context_lens, float scale,
+                                            const photon_decode_desc *desc, void *out,
+                                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (desc && desc->num_seqs > 0) {
+        if (!k_new || !v_new)
+            return fail(PHOTON_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+        if (!aligned16(k_new) || !aligned16(v_new))
+            return fail(PHOTON_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    }
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, desc,
+                       out, workspace, workspace_bytes, stream);
 }
 
 const char *photon_status_str(photon_status status)

@@ -289,3 +289,15 @@ def test_multi_query_with_nothing_to_do_launches_nothing():
     assert _mq(mqd(b=0, t=0, mq=0), q=None, kc=None, vc=None, tables=None, lens=None, qs=None,
                out=None) == pa.OK
     assert _mq(mqd(t=0, mq=0), q=None, out=None) == pa.OK
+
+
+def test_decode_step_rejects_missing_new_rows():
+    d = dd(part=256)
+    need = pa.workspace_bytes(d)
+    call = lambda kn, vn: pa.lib.photon_paged_attn_decode_step(FAKE, kn, vn, FAKE, FAKE, FAKE, FAKE,
+                                                               0.125, ctypes.byref(d), FAKE, FAKE,
+                                                               need, None)
+    assert call(None, FAKE) == pa.ERR_INVALID_ARG
+    assert call(FAKE, FAKE + 4) == pa.ERR_INVALID_ARG
+    assert pa.lib.photon_paged_attn_decode_step(None, None, None, None, None, None, None, 0.125,
+                                                ctypes.byref(dd(b=0)), None, None, 0, None) == pa.OK

@@ -324,3 +324,86 @@ def test_hip_graph_replays_match_eager(pa):
                                      max_context_len=lay.max_context_len, workspace=ws)
         torch.cuda.synchronize()
         assert host(other).tobytes() == host(eager).tobytes()
+
+
+# --------------------------------------------------------- fused decode step
+
+def derived_slots(tables, ctx, bs=16):
+    """Slot of position ctx-1 of each sequence (-1 for an empty context)."""
+    out = np.full(len(ctx), -1, np.int32)
+    for b, c in enumerate(ctx):
+        if c > 0:
+            out[b] = tables[b, (c - 1) // bs] * bs + (c - 1) % bs
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b_b1", "llama1b_b16", "cb_b64", "llama1b_b16_bf16"])
+def test_fused_step_equals_write_then_decode(pa, name):
+    cfg = di.CONFIGS[name]
+    lay = di.make_layout(cfg)
+    t = di.make_layer(cfg, lay, 1)
+    slots = derived_slots(lay.block_tables, lay.context_lens)
+    assert (slots == lay.slot_mapping).all()
+    ek, ev = oracle.kv_cache_write(t.k_new, t.v_new, slots, t.k_cache, t.v_cache)
+    ref = oracle.paged_attn_decode(t.q, ek, ev, lay.block_tables, lay.context_lens, cfg.scale)
+    q, kn, vn = dev(t.q), dev(t.k_new), dev(t.v_new)
+    tables, lens = dev(lay.block_tables), dev(lay.context_lens)
+    # fused
+    gk, gv = dev(t.k_cache), dev(t.v_cache)
+    fused = pa.paged_attn_decode_step(q, kn, vn, gk, gv, tables, lens, cfg.scale,
+                                      max_context_len=lay.max_context_len)
+    # unfused: the cache-write kernel, then the decode kernel
+    uk, uv = dev(t.k_cache), dev(t.v_cache)
+    pa.kv_cache_write(kn, vn, dev(slots), uk, uv)
+    unfused = pa.paged_attn_decode(q, uk, uv, tables, lens, cfg.scale,
+                                   max_context_len=lay.max_context_len)
+    torch.cuda.synchronize()
+    assert host(gk).tobytes() == ek.tobytes() and host(gv).tobytes() == ev.tobytes()
+    assert host(fused).tobytes() == host(unfused).tobytes()
+    assert_close(host(fused), ref, cfg.np_dtype, name)
+
+
+@pytest.mark.parametrize("part", [0, 32, 64, 128, 512])
+def test_fused_step_ragged_batch_and_partitions(pa, part):
+    # empty contexts, contexts ending on a block boundary, and partition
+    # sizes that put a segment's last chunk in the middle of a wave's slice
+    rng = np.random.default_rng(31)
+    ctx = [0, 1, 16, 17, 31, 32, 33, 300, 0, 1000, 64, 2]
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 0, 32, 8, 64, ctx_list=ctx, spare=5)
+    kn = rng.standard_normal((len(ctx), 8, 64)).astype(np.float32)
+    vn = rng.standard_normal((len(ctx), 8, 64)).astype(np.float32)
+    slots = derived_slots(tables, ctx)
+    ek, ev = oracle.kv_cache_write(kn, vn, slots, kc, vc)
+    ref = oracle.paged_attn_decode(q, ek, ev, tables, ctx, 0.125)
+    gk, gv = dev(kc), dev(vc)
+    out = pa.paged_attn_decode_step(dev(q), dev(kn), dev(vn), gk, gv, dev(tables), dev(ctx), 0.125,
+                                    max_context_len=int(ctx.max()), partition_tokens=part)
+    torch.cuda.synchronize()
+    assert host(gk).tobytes() == ek.tobytes() and host(gv).tobytes() == ev.tobytes()
+    got = host(out)
+    assert_close(got, ref, np.float32, f"partition {part}")
+    assert (got[0] == 0).all() and (got[8] == 0).all()
+
+
+def test_fused_step_graph_replays_match_eager(pa):
+    cfg = di.CONFIGS["cb_b64"]
+    lay = di.make_layout(cfg)
+    t = di.make_layer(cfg, lay)
+    q, kn, vn = dev(t.q), dev(t.k_new), dev(t.v_new)
+    tables, lens = dev(lay.block_tables), dev(lay.context_lens)
+    desc = pa.decode_desc(q, dev(t.k_cache), tables, lay.max_context_len)
+    ws = pa.new_workspace(pa.workspace_bytes(desc), "cuda:0")
+    kc, vc = dev(t.k_cache), dev(t.v_cache)
+    eager = pa.paged_attn_decode_step(q, kn, vn, kc, vc, tables, lens, cfg.scale,
+                                      max_context_len=lay.max_context_len, workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(q)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pa.paged_attn_decode_step(q, kn, vn, kc, vc, tables, lens, cfg.scale,
+                                  max_context_len=lay.max_context_len, out=out, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert host(out).tobytes() == host(eager).tobytes(), f"replay {rep} differs"
