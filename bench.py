@@ -281,11 +281,15 @@ def multi_query_measurements(args, cfg, lay, layers, device, stream):
     qv = [di.to_torch(di.cast(rng.standard_normal((b * n, cfg.num_q_heads, cfg.head_dim)),
                               cfg.np_dtype)).to(device) for _ in range(2)]
     outs = [torch.empty_like(qv[0]) for _ in range(2)]
+    max_ctx = lay.max_context_len
+    mqd = pa.multi_query_desc(qv[0], layers[0]["kc"], tables, b, n, max_ctx)
+    mq_ws = pa.new_workspace(pa.multi_query_workspace_bytes(mqd), device)
 
     def verify_burst():
         for i, L in enumerate(layers):
             pa.paged_attn_multi_query(qv[i % 2], L["kc"], L["vc"], tables, lens, qs, cfg.scale,
-                                      max_query_len=n, out=outs[i % 2])
+                                      max_query_len=n, max_context_len=max_ctx, out=outs[i % 2],
+                                      workspace=mq_ws)
 
     verify_burst()
     torch.cuda.synchronize()
@@ -326,13 +330,16 @@ def multi_query_measurements(args, cfg, lay, layers, device, stream):
     out = torch.empty_like(q)
     tab_t, ctx_t = di.to_torch(tab).to(device), torch.tensor(ctx, dtype=torch.int32, device=device)
     qs_t = di.to_torch(qstart).to(device)
+    pf_kw = dict(max_query_len=512, max_context_len=max(ctx), out=out)
+    pfd = pa.multi_query_desc(q, kc, tab_t, 4, 512, max(ctx))
+    pf_kw["workspace"] = pa.new_workspace(pa.multi_query_workspace_bytes(pfd), device)
     for _ in range(2):
-        pa.paged_attn_multi_query(q, kc, vc, tab_t, ctx_t, qs_t, cfg.scale, max_query_len=512, out=out)
+        pa.paged_attn_multi_query(q, kc, vc, tab_t, ctx_t, qs_t, cfg.scale, **pf_kw)
     torch.cuda.synchronize()
     reps = max(args.steps, 5)
     a.record(stream)
     for _ in range(reps):
-        pa.paged_attn_multi_query(q, kc, vc, tab_t, ctx_t, qs_t, cfg.scale, max_query_len=512, out=out)
+        pa.paged_attn_multi_query(q, kc, vc, tab_t, ctx_t, qs_t, cfg.scale, **pf_kw)
     z.record(stream)
     torch.cuda.synchronize()
     prefill_us = a.elapsed_time(z) * 1e3 / reps

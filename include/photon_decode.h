@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PHOTON_ABI_VERSION 5
+#define PHOTON_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define PHOTON_API __attribute__((visibility("default")))
@@ -140,9 +140,24 @@ typedef struct photon_multi_query_desc {
     int32_t max_blocks_per_seq; /* row length of block_tables, > 0                */
     int32_t max_query_len;      /* >= every query_start[b+1] - query_start[b];
                                    sizes the grid                                 */
+    int32_t max_context_len;    /* >= every context_lens[b], <= max_blocks_per_seq
+                                   * block_size; sizes the KV splits              */
+    int32_t split_tokens;       /* 0 = automatic (about 1024 workgroups); else the
+                                   KV tokens one workgroup scans for a tile of 16
+                                   query rows, a positive multiple of 64          */
     int32_t flags;              /* PHOTON_DECODE_OUT_F32 or 0                     */
     photon_kv_desc kv;
 } photon_multi_query_desc;
+
+/*
+ * Workspace bytes photon_paged_attn_multi_query needs for desc: 0 when no
+ * tile's KV range is split, else one int32 arrival counter per tile of 16
+ * query rows, then one fp32 record of 16 * (head_dim + 2) floats per tile
+ * and split.  Zero-filled once before first use; every completed call leaves
+ * the counters at zero.  Concurrent calls need workspaces of their own.
+ */
+PHOTON_API photon_status photon_paged_attn_multi_query_workspace_bytes(
+    const photon_multi_query_desc *desc, size_t *bytes);
 
 /*
  * Multi-query paged attention with a causal tail: several new tokens of each
@@ -173,8 +188,13 @@ typedef struct photon_multi_query_desc {
  *   out           [num_tokens, num_q_heads, head_dim]     kv.dtype (fp32 with
  *                 PHOTON_DECODE_OUT_F32), 16-byte aligned
  *
- * No workspace.  Device-resident indices are not range-checked (caller
- * error).  num_seqs == 0 or num_tokens == 0 launches nothing.
+ *   workspace     device scratch of at least the size the workspace query
+ *                 returns (may be NULL when that is 0), 16-byte aligned
+ *
+ * A tile of 16 query rows whose causal range spans several splits is
+ * reduced by the last of its workgroups to finish, in split order, so
+ * results are deterministic.  Device-resident indices are not range-checked
+ * (caller error).  num_seqs == 0 or num_tokens == 0 launches nothing.
  */
 PHOTON_API photon_status photon_paged_attn_multi_query(const void *q, const void *k_cache,
                                                        const void *v_cache,
@@ -182,7 +202,8 @@ PHOTON_API photon_status photon_paged_attn_multi_query(const void *q, const void
                                                        const int32_t *context_lens,
                                                        const int32_t *query_start, float scale,
                                                        const photon_multi_query_desc *desc,
-                                                       void *out, void *stream);
+                                                       void *out, void *workspace,
+                                                       size_t workspace_bytes, void *stream);
 
 /* Rotary embedding parameters of photon_rope_kv_cache_write. */
 typedef struct photon_rope_desc {

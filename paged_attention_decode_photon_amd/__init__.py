@@ -61,7 +61,8 @@ class DecodeDesc(ctypes.Structure):
 class MultiQueryDesc(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("max_query_len", ctypes.c_int32), ("flags", ctypes.c_int32), ("kv", KvDesc)]
+                ("max_query_len", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("split_tokens", ctypes.c_int32), ("flags", ctypes.c_int32), ("kv", KvDesc)]
 
 
 class RopeDesc(ctypes.Structure):
@@ -93,7 +94,10 @@ def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.photon_kv_cache_write.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.POINTER(KvDesc), vp]
     lib.photon_kv_cache_write.restype = st
     lib.photon_paged_attn_multi_query.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float,
-                                                  ctypes.POINTER(MultiQueryDesc), vp, vp]
+                                                  ctypes.POINTER(MultiQueryDesc), vp, vp, sz, vp]
+    lib.photon_paged_attn_multi_query_workspace_bytes.argtypes = [ctypes.POINTER(MultiQueryDesc),
+                                                                  ctypes.POINTER(sz)]
+    lib.photon_paged_attn_multi_query_workspace_bytes.restype = st
     lib.photon_paged_attn_multi_query.restype = st
     lib.photon_rope_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp,
                                                ctypes.POINTER(KvDesc), ctypes.POINTER(RopeDesc), vp]
@@ -299,15 +303,32 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
     return out
 
 
+def multi_query_desc(q, k_cache, block_tables, num_seqs: int, max_query_len: int,
+                     max_context_len: int, split_tokens: int = 0, flags: int = 0) -> MultiQueryDesc:
+    return MultiQueryDesc(num_seqs, q.shape[0], q.shape[1], block_tables.shape[1],
+                          int(max_query_len), int(max_context_len), int(split_tokens), int(flags),
+                          kv_desc(k_cache))
+
+
+def multi_query_workspace_bytes(desc: MultiQueryDesc) -> int:
+    n = ctypes.c_size_t(0)
+    check(lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
 def paged_attn_multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start,
-                           scale: float, max_query_len: int | None = None, out=None,
-                           out_dtype=None):
+                           scale: float, max_query_len: int | None = None,
+                           max_context_len: int | None = None, out=None, out_dtype=None,
+                           workspace=None, split_tokens: int = 0):
     """Causal multi-query paged attention (chunked prefill / speculative verification).
 
     q, out: [T, Hq, D]; sequence b owns rows query_start[b] .. query_start[b+1]-1,
     the last tokens of its context_lens[b]; row j attends to positions
     <= context_lens[b] - n_b + j.  ``max_query_len`` bounds every n_b (read
-    back from the device, with a synchronisation, if None).
+    back from the device, with a synchronisation, if None), and
+    ``max_context_len`` every context length (likewise).  ``split_tokens``
+    (0 = automatic) is the KV range one workgroup scans per 16-row tile;
+    ``workspace`` is allocated through torch when needed and not given.
     """
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
@@ -324,6 +345,8 @@ def paged_attn_multi_query(q, k_cache, v_cache, block_tables, context_lens, quer
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
     if max_query_len is None:
         max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if b else 0
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if b else 0
     if out is not None:
         out_dtype = out.dtype
     elif out_dtype is None:
@@ -338,12 +361,17 @@ def paged_attn_multi_query(q, k_cache, v_cache, block_tables, context_lens, quer
         _contig("out", out)
         if out.shape != q.shape:
             raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape")
-    desc = MultiQueryDesc(b, q.shape[0], q.shape[1], block_tables.shape[1], int(max_query_len),
-                          flags, kv_desc(k_cache))
+    desc = multi_query_desc(q, k_cache, block_tables, b, max_query_len, max_context_len,
+                            split_tokens, flags)
+    ws_need = multi_query_workspace_bytes(desc)
+    if ws_need and workspace is None:
+        workspace = new_workspace(ws_need, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(lib.photon_paged_attn_multi_query(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                             block_tables.data_ptr(), context_lens.data_ptr(),
                                             query_start.data_ptr(), float(scale), ctypes.byref(desc),
-                                            out.data_ptr(), _stream_ptr(q)))
+                                            out.data_ptr(), ws_ptr, ws_len, _stream_ptr(q)))
     return out
 
 

@@ -94,6 +94,10 @@ struct MultiQueryArgs {
     int head_dim;
     int max_blocks;
     int max_tiles;  // ceil(max_query_len * group / 16): grid x
+    int split_blocks;  // KV blocks per split of a tile's causal range
+    int num_splits;    // grid z: splits of the longest range
+    int *ws_count;     // [B * Hkv * max_tiles] arrival counters, zero between calls
+    float *ws_rec;     // [B * Hkv * max_tiles * num_splits] records of 16 * (D + 2) floats
     int dtype;
     int out_f32;
     float qscale;   // scale * log2(e)

@@ -12,9 +12,17 @@
 //
 // Work decomposition.  The n_b * G query rows of one (sequence, KV head)
 // are ordered token-major (row = j * G + head offset) and cut into tiles of
-// 16 rows; a workgroup of four waves takes one tile, each wave taking every
-// fourth 16-token KV block of the tile's causal range, and the four partial
-// softmax states are merged through LDS at the end.
+// 16 rows.  A tile's causal range of KV blocks is cut into splits of
+// split_blocks blocks (grid z); a workgroup of four waves takes one split of
+// one tile, each wave taking every fourth block, and the four partial
+// softmax states are merged through LDS.  A tile with one split writes its
+// rows directly.  Otherwise each workgroup stores its (max, sum, unnormalised
+// rows) record with device-scope stores, waits for them, and counts its
+// arrival on the tile's counter; the workgroup that completes the count
+// merges the records in split order (deterministic) and resets the counter.
+// Records cross XCDs, whose L2 caches are not coherent with each other, so
+// they are written and read with device-scope (sc1) buffer accesses rather
+// than behind cache-wide fences.
 //
 // Matrix-core mapping (16x16 MFMA, K = 16 for 16-bit storage, K = 4 for
 // fp32).  Per KV block the wave forms S^T = K Q^T (16 tokens x 16 rows):
@@ -47,6 +55,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMqWaves = 4;
+constexpr int kSc1 = 16;  // cache-policy bits of device-scope record accesses
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(float *rec, int floats)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(rec, (short)0, floats * 4, 0x00020000);
+}
 constexpr int kRawWord3 = 0x00020000;
 constexpr int kTile = 16;  // query rows per tile, tokens per KV block
 
@@ -99,6 +113,28 @@ __device__ __forceinline__ f32x4 mfma16(const u32x2 &a, const u32x2 &b, f32x4 c)
                                                          __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 
+// Workgroup-level running max and exponential sum of tile row r, from the
+// four waves' statistics (the same values every lane forms in the merge).
+__device__ __forceinline__ float m_all_row(const float (&sm)[kMqWaves][kTile], int r)
+{
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMqWaves; ++w)
+        m = fmaxf(m, sm[w][r]);
+    return m;
+}
+__device__ __forceinline__ float l_all_row(const float (&sm)[kMqWaves][kTile],
+                                           const float (&sl)[kMqWaves][kTile], int r)
+{
+    const float m = m_all_row(sm, r);
+    const float mu = m == -INFINITY ? 0.0f : m;
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMqWaves; ++w)
+        l += sl[w][r] * __builtin_amdgcn_exp2f(sm[w][r] - mu);
+    return l;
+}
+
 template <typename T, typename O, int D, int G>
 __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs a)
 {
@@ -133,6 +169,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     const int last_row = min(tile * kTile + kTile - 1, rows - 1);
     const int scan_end = first_pos + last_row / G + 1;  // tokens [0, scan_end)
     const int nblk = (scan_end + kTile - 1) / kTile;
+    const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
+    const int z = blockIdx.z;
+    if (z >= nsplit)
+        return;  // this tile's range has fewer splits
+    const int n_begin = z * a.split_blocks;
+    const int n_end = min(nblk, n_begin + a.split_blocks);
 
     const int r = tile * kTile + lr;  // this lane's row
     const bool row_ok = r < rows;
@@ -166,16 +208,16 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     T *vt = reinterpret_cast<T *>(smem + wave * VT_BYTES);
     const size_t tile_elems = (size_t)kTile * D;
 
-    for (int n = wave; n < nblk; n += kMqWaves) {
+    // Issue the K and V loads of block n (zero rows when !live).
+    auto load_block = [&](int n, bool live, uint32_t (&kw)[NW], uint32_t (&vw)[NW]) {
         const int blk = __builtin_amdgcn_readfirstlane(a.block_tables[(size_t)b * a.max_blocks + n]);
-        const int valid = min(kTile, scan_end - n * kTile);
+        const int valid = live ? min(kTile, scan_end - n * kTile) : 0;
         const size_t base = ((size_t)blk * hkv + g) * tile_elems;
         const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const T *)a.k_cache + base), (short)0, valid * D * EB, kRawWord3);
         const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const T *)a.v_cache + base), (short)0, valid * D * EB, kRawWord3);
         const int off = (lr * D + gq * QD) * EB;
-        uint32_t kw[NW], vw[NW];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const u32x4 kv = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16 * i, 0, 0);
@@ -186,7 +228,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
                 vw[4 * i + k] = vv[k];
             }
         }
+    };
 
+    // Scores, softmax update and P.V of block n from its loaded K and V.
+    auto compute_block = [&](int n, const uint32_t (&kw)[NW], const uint32_t (&vw)[NW]) {
         // S^T = K Q^T for this block.
         f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (EB == 4) {
@@ -267,6 +312,19 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
             }
         }
         wave_sync();  // reads of the V tile are done before the next block overwrites it
+    };
+
+    // Two of this wave's blocks per step, both loaded before either is used,
+    // so each wave keeps two blocks of K and V in flight.
+    for (int n = n_begin + wave; n < n_end; n += 2 * kMqWaves) {
+        const int n2 = n + kMqWaves;
+        const bool two = n2 < n_end;
+        uint32_t ka[NW], va[NW], kb[NW], vb[NW];
+        load_block(n, true, ka, va);
+        load_block(two ? n2 : n, two, kb, vb);
+        compute_block(n, ka, va);
+        if (two)
+            compute_block(n2, kb, vb);
     }
 
     // Merge the four waves' partial states of each row.
@@ -277,16 +335,13 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         stat_l[wave][lr] = l_row;
     }
     __syncthreads();  // also ends every wave's use of the V tiles
-    float m_all = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMqWaves; ++w)
-        m_all = fmaxf(m_all, stat_m[w][lr]);
-    float l_all = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kMqWaves; ++w)
-        l_all += stat_l[w][lr] * __builtin_amdgcn_exp2f(stat_m[w][lr] - m_all);
-    // every row has token 0 in range, so m_all is finite and l_all > 0
-    const float f = __builtin_amdgcn_exp2f(m_run - m_all) / l_all;
+    const float m_all = m_all_row(stat_m, lr);
+    const float l_all = l_all_row(stat_m, stat_l, lr);
+    // With one split every real row has token 0 in range, so m_all is finite
+    // and l_all > 0; with several, a split's rows may all be masked (m_all =
+    // -inf, l_all = 0): the record carries that and the merge weighs it 0.
+    const float m_use = m_all == -INFINITY ? 0.0f : m_all;
+    const float f = __builtin_amdgcn_exp2f(m_run - m_use) / (nsplit == 1 ? l_all : 1.0f);
     float *ob = reinterpret_cast<float *>(smem) + wave * kTile * D;
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -295,14 +350,13 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
             ob[lr * D + 16 * t + 4 * gq + i] = o_acc[t][i] * f;
     __syncthreads();
 
-    // Sum the four partial rows and store: thread -> (row, D/16 columns).
+    // Sum the four partial rows: thread -> (row, D/16 columns).
     constexpr int PER = D / 16;
     const int orow = threadIdx.x >> 4;
     const int c0 = (threadIdx.x & 15) * PER;
     const int rr = tile * kTile + orow;
-    if (rr < rows) {
-        const int oj = rr / G, oh = rr - (rr / G) * G;
-        float v[PER];
+    float v[PER];
+    {
         const float *o0 = reinterpret_cast<const float *>(smem);
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
@@ -312,17 +366,90 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
                 acc += o0[(w * kTile + orow) * D + c0 + e];
             v[e] = acc;
         }
-        O *dst = (O *)a.out + ((size_t)(q0 + oj) * hq + (size_t)g * G + oh) * D + c0;
+    }
+    O *dst = (O *)a.out + ((size_t)(q0 + (rr / G)) * hq + (size_t)g * G + (rr % G)) * D + c0;
+    if (nsplit == 1) {
+        if (rr < rows) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                dst[e] = Elem<O>::from_float(v[e]);
+        }
+        return;
+    }
+
+    // Several splits: record = o[16][D] (unnormalised), m[16], l[16].
+    constexpr int REC = kTile * D + 2 * kTile;
+    const size_t tile_id = ((size_t)blockIdx.y * gridDim.x + tile);
+    {
+        float *rec = a.ws_rec + (tile_id * gridDim.z + z) * REC;
+        const __amdgpu_buffer_rsrc_t rs = rec_rsrc(rec, REC);
+#pragma unroll
+        for (int k = 0; k < PER / 4; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                      __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])},
+                rs, (orow * D + c0 + 4 * k) * 4, 0, kSc1);
+        if ((threadIdx.x & 15) == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_all_row(stat_m, orow)), rs,
+                                                  (kTile * D + orow) * 4, 0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_all_row(stat_m, stat_l, orow)),
+                                                  rs, (kTile * D + kTile + orow) * 4, 0, kSc1);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's record stores are done
+    __syncthreads();                                   // ... and every thread's
+    __shared__ int arrived;
+    if (threadIdx.x == 0)
+        arrived = __hip_atomic_fetch_add(&a.ws_count[tile_id], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) + 1;
+    __syncthreads();
+    if (arrived != nsplit)
+        return;
+
+    // Last arrival: merge the splits in order.
+    asm volatile("" ::: "memory");
+    if (rr < rows) {
+        float mz_max = -INFINITY;
+        for (int zz = 0; zz < nsplit; ++zz) {
+            const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a.ws_rec + (tile_id * gridDim.z + zz) * REC, REC);
+            mz_max = fmaxf(mz_max, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                       rs, (kTile * D + orow) * 4, 0, kSc1)));
+        }
+        float lsum = 0.0f, acc[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-            dst[e] = Elem<O>::from_float(v[e]);
+            acc[e] = 0.0f;
+        for (int zz = 0; zz < nsplit; ++zz) {
+            const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a.ws_rec + (tile_id * gridDim.z + zz) * REC, REC);
+            const float mz = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rs, (kTile * D + orow) * 4, 0, kSc1));
+            const float lz = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rs, (kTile * D + kTile + orow) * 4, 0, kSc1));
+            const float wz = mz == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mz - mz_max);
+            lsum = __builtin_fmaf(wz, lz, lsum);
+#pragma unroll
+            for (int k = 0; k < PER / 4; ++k) {
+                const u32x4 oz = __builtin_amdgcn_raw_buffer_load_b128(rs, (orow * D + c0 + 4 * k) * 4,
+                                                                      0, kSc1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[4 * k + e] = __builtin_fmaf(wz, __uint_as_float(oz[e]), acc[4 * k + e]);
+            }
+        }
+        const float inv = 1.0f / lsum;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            dst[e] = Elem<O>::from_float(acc[e] * inv);
     }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&a.ws_count[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, typename O, int D>
 hipError_t launch_mq_group(const MultiQueryArgs &a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.num_seqs * a.num_kv_heads));
+    const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.num_seqs * a.num_kv_heads),
+                    (unsigned)a.num_splits);
     const dim3 block(kMqWaves * 64);
     switch (a.group) {
     case 1: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 1>), grid, block, 0, stream, a); break;

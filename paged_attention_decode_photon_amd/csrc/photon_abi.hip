@@ -179,6 +179,86 @@ photon_status plan_decode(const photon_decode_desc *d, Plan *plan)
     return PHOTON_OK;
 }
 
+struct MqPlan {
+    int group;
+    int max_tiles;
+    int split_blocks;
+    int num_splits;
+    size_t count_bytes;
+    size_t ws_bytes;
+};
+
+// Automatic KV splitting of the multi-query kernel aims at this many
+// workgroups (four per compute unit of an MI355X).
+constexpr int64_t kMqTargetGroups = 1024;
+// ... but no split shorter than 32 blocks: each wave then runs at least four
+// blocks, two at a time (measured best for 4-token verification at batch 16).
+constexpr int64_t kMqMinSplitBlocks = 32;
+
+photon_status plan_multi_query(const photon_multi_query_desc *d, MqPlan *plan)
+{
+    if (!d)
+        return fail(PHOTON_ERR_INVALID_ARG, "multi-query descriptor is NULL");
+    photon_status st = check_kv(&d->kv);
+    if (st != PHOTON_OK)
+        return st;
+    if (d->num_seqs < 0 || d->num_tokens < 0 || d->num_q_heads <= 0 || d->max_blocks_per_seq <= 0 ||
+        d->max_query_len < 0 || d->max_context_len < 0 || d->split_tokens < 0)
+        return fail(PHOTON_ERR_INVALID_ARG,
+                    "bad sizes (num_seqs=%d num_tokens=%d num_q_heads=%d max_blocks_per_seq=%d "
+                    "max_query_len=%d max_context_len=%d split_tokens=%d)",
+                    d->num_seqs, d->num_tokens, d->num_q_heads, d->max_blocks_per_seq,
+                    d->max_query_len, d->max_context_len, d->split_tokens);
+    if (d->flags & ~kKnownDecodeFlags)
+        return fail(PHOTON_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)d->flags);
+    if (d->num_q_heads % d->kv.num_kv_heads != 0)
+        return fail(PHOTON_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    d->num_q_heads, d->kv.num_kv_heads);
+    const int group = d->num_q_heads / d->kv.num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return fail(PHOTON_ERR_UNSUPPORTED, "query heads per KV head %d not built (1, 2, 4, 8 are)",
+                    group);
+    if ((int64_t)d->num_seqs * d->kv.num_kv_heads > 65535)
+        return fail(PHOTON_ERR_UNSUPPORTED, "num_seqs * num_kv_heads %lld above 65535",
+                    (long long)d->num_seqs * d->kv.num_kv_heads);
+    if (d->max_query_len > d->num_tokens)
+        return fail(PHOTON_ERR_INVALID_ARG, "max_query_len %d exceeds num_tokens %d",
+                    d->max_query_len, d->num_tokens);
+    if ((int64_t)d->max_context_len > (int64_t)d->max_blocks_per_seq * d->kv.block_size)
+        return fail(PHOTON_ERR_INVALID_ARG,
+                    "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
+                    d->max_context_len, (long long)d->max_blocks_per_seq * d->kv.block_size);
+    if (d->split_tokens % 64 != 0)
+        return fail(PHOTON_ERR_INVALID_ARG, "split_tokens %d is not a multiple of 64",
+                    d->split_tokens);
+    MqPlan p{};
+    p.group = group;
+    p.max_tiles = (int)(((int64_t)d->max_query_len * group + 15) / 16);
+    const int64_t tiles = (int64_t)d->num_seqs * d->kv.num_kv_heads * p.max_tiles;
+    const int64_t max_nblk = ((int64_t)d->max_context_len + d->kv.block_size - 1) / d->kv.block_size;
+    int64_t sb;
+    if (d->split_tokens > 0) {
+        sb = d->split_tokens / d->kv.block_size;
+    } else {
+        const int64_t want = tiles > 0 ? (kMqTargetGroups + tiles - 1) / tiles : 1;
+        sb = want > 1 ? (max_nblk + want - 1) / want : max_nblk;
+        sb = (sb + 7) / 8 * 8;  // whole steps: four waves, two blocks each
+        sb = sb < kMqMinSplitBlocks ? kMqMinSplitBlocks : sb;
+    }
+    const int64_t splits = max_nblk > sb ? (max_nblk + sb - 1) / sb : 1;
+    if (splits > 65535)
+        return fail(PHOTON_ERR_UNSUPPORTED, "%lld KV splits, at most 65535", (long long)splits);
+    p.split_blocks = (int)(sb > INT32_MAX ? INT32_MAX : sb);
+    p.num_splits = (int)splits;
+    if (splits > 1 && tiles > 0) {
+        const size_t rec = (size_t)16 * (d->kv.head_dim + 2) * sizeof(float);
+        p.count_bytes = align256((size_t)tiles * sizeof(int));
+        p.ws_bytes = p.count_bytes + (size_t)tiles * splits * rec;
+    }
+    *plan = p;
+    return PHOTON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,38 +289,29 @@ photon_status photon_kv_cache_write(const void *k, const void *v, const int32_t 
     return ok();
 }
 
+photon_status photon_paged_attn_multi_query_workspace_bytes(const photon_multi_query_desc *d,
+                                                           size_t *bytes)
+{
+    if (!bytes)
+        return fail(PHOTON_ERR_INVALID_ARG, "bytes is NULL");
+    MqPlan p;
+    photon_status st = plan_multi_query(d, &p);
+    if (st != PHOTON_OK)
+        return st;
+    *bytes = p.ws_bytes;
+    return ok();
+}
+
 photon_status photon_paged_attn_multi_query(const void *q, const void *k_cache, const void *v_cache,
                                            const int32_t *block_tables, const int32_t *context_lens,
                                            const int32_t *query_start, float scale,
-                                           const photon_multi_query_desc *d, void *out, void *stream)
+                                           const photon_multi_query_desc *d, void *out,
+                                           void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (!d)
-        return fail(PHOTON_ERR_INVALID_ARG, "multi-query descriptor is NULL");
-    photon_status st = check_kv(&d->kv);
+    MqPlan p;
+    photon_status st = plan_multi_query(d, &p);
     if (st != PHOTON_OK)
         return st;
-    if (d->num_seqs < 0 || d->num_tokens < 0 || d->num_q_heads <= 0 || d->max_blocks_per_seq <= 0 ||
-        d->max_query_len < 0)
-        return fail(PHOTON_ERR_INVALID_ARG,
-                    "bad sizes (num_seqs=%d num_tokens=%d num_q_heads=%d max_blocks_per_seq=%d "
-                    "max_query_len=%d)",
-                    d->num_seqs, d->num_tokens, d->num_q_heads, d->max_blocks_per_seq,
-                    d->max_query_len);
-    if (d->flags & ~kKnownDecodeFlags)
-        return fail(PHOTON_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)d->flags);
-    if (d->num_q_heads % d->kv.num_kv_heads != 0)
-        return fail(PHOTON_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
-                    d->num_q_heads, d->kv.num_kv_heads);
-    const int group = d->num_q_heads / d->kv.num_kv_heads;
-    if (group != 1 && group != 2 && group != 4 && group != 8)
-        return fail(PHOTON_ERR_UNSUPPORTED, "query heads per KV head %d not built (1, 2, 4, 8 are)",
-                    group);
-    if ((int64_t)d->num_seqs * d->kv.num_kv_heads > 65535)
-        return fail(PHOTON_ERR_UNSUPPORTED, "num_seqs * num_kv_heads %lld above 65535",
-                    (long long)d->num_seqs * d->kv.num_kv_heads);
-    if (d->max_query_len > d->num_tokens)
-        return fail(PHOTON_ERR_INVALID_ARG, "max_query_len %d exceeds num_tokens %d",
-                    d->max_query_len, d->num_tokens);
     if (!std::isfinite(scale))
         return fail(PHOTON_ERR_INVALID_ARG, "scale is not finite");
     if (d->num_seqs == 0 || d->num_tokens == 0 || d->max_query_len == 0)
@@ -251,6 +322,11 @@ photon_status photon_paged_attn_multi_query(const void *q, const void *k_cache, 
         return fail(PHOTON_ERR_INVALID_ARG, "q, the pools and out must be 16-byte aligned");
     if (!aligned4(block_tables) || !aligned4(context_lens) || !aligned4(query_start))
         return fail(PHOTON_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
+    if (workspace_bytes < p.ws_bytes)
+        return fail(PHOTON_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    p.ws_bytes);
+    if (p.ws_bytes && (!workspace || !aligned16(workspace)))
+        return fail(PHOTON_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
     photon::MultiQueryArgs a{};
     a.q = q;
     a.k_cache = k_cache;
@@ -261,10 +337,15 @@ photon_status photon_paged_attn_multi_query(const void *q, const void *k_cache, 
     a.out = out;
     a.num_seqs = d->num_seqs;
     a.num_kv_heads = d->kv.num_kv_heads;
-    a.group = group;
+    a.group = p.group;
     a.head_dim = d->kv.head_dim;
     a.max_blocks = d->max_blocks_per_seq;
-    a.max_tiles = (int)(((int64_t)d->max_query_len * group + 15) / 16);
+    a.max_tiles = p.max_tiles;
+    a.split_blocks = p.split_blocks;
+    a.num_splits = p.num_splits;
+    char *ws = static_cast<char *>(workspace);
+    a.ws_count = p.ws_bytes ? reinterpret_cast<int *>(ws) : nullptr;
+    a.ws_rec = p.ws_bytes ? reinterpret_cast<float *>(ws + p.count_bytes) : nullptr;
     a.dtype = d->kv.dtype;
     a.out_f32 = (d->flags & PHOTON_DECODE_OUT_F32) ? 1 : 0;
     a.qscale = (float)((double)scale * 1.4426950408889634);  // log2(e)

@@ -249,14 +249,35 @@ def test_scheduler_structs_match_the_header(tmp_path):
                    ctypes.sizeof(sched.SchedRequestInfo), sched.SchedRequestInfo.num_preemptions.offset]
 
 
-def _mq(desc, q=FAKE, kc=FAKE, vc=FAKE, tables=FAKE, lens=FAKE, qs=FAKE, scale=0.125, out=FAKE):
+def _mq(desc, q=FAKE, kc=FAKE, vc=FAKE, tables=FAKE, lens=FAKE, qs=FAKE, scale=0.125, out=FAKE,
+        ws=FAKE, ws_bytes=1 << 30):
     return pa.lib.photon_paged_attn_multi_query(q, kc, vc, tables, lens, qs, scale,
                                                 ctypes.byref(desc) if desc is not None else None,
-                                                out, None)
+                                                out, ws, ws_bytes, None)
 
 
-def mqd(b=4, t=16, hq=32, mb=8, mq=4, flags=0, **kw):
-    return pa.MultiQueryDesc(b, t, hq, mb, mq, flags, kv(**kw))
+def mqd(b=4, t=16, hq=32, mb=8, mq=4, maxctx=100, split=0, flags=0, **kw):
+    return pa.MultiQueryDesc(b, t, hq, mb, mq, maxctx, split, flags, kv(**kw))
+
+
+def test_multi_query_split_and_workspace_formula():
+    # 4 seqs x 8 KV heads x ceil(4*4/16)=1 tile = 32 tiles; 2000 tokens = 125 blocks
+    d = mqd(mb=128, maxctx=2000)
+    n = ctypes.c_size_t(0)
+    assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    # automatic: 1024 / 32 = 32 splits wanted -> 4 blocks each, raised to the
+    # 32-block minimum -> ceil(125/32) = 4 splits
+    counters = (32 * 4 + 255) // 256 * 256
+    rec = 16 * (64 + 2) * 4
+    assert n.value == counters + 32 * 4 * rec
+    # explicit 512-token splits: 4 splits of 32 blocks
+    d = mqd(mb=128, maxctx=2000, split=512)
+    assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == counters + 32 * 4 * rec
+    # one split covers everything: no workspace
+    d = mqd(mb=128, maxctx=2000, split=2048)
+    assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 0
 
 
 @pytest.mark.parametrize("desc,code", [
@@ -271,6 +292,10 @@ def mqd(b=4, t=16, hq=32, mb=8, mq=4, flags=0, **kw):
     (mqd(b=9000), pa.ERR_UNSUPPORTED),          # grid y limit with 8 KV heads
     (mqd(d=80), pa.ERR_UNSUPPORTED),
     (mqd(dtype=9), pa.ERR_INVALID_ARG),
+    (mqd(maxctx=8 * 16 + 1), pa.ERR_INVALID_ARG),   # past the tables
+    (mqd(maxctx=-1), pa.ERR_INVALID_ARG),
+    (mqd(split=100), pa.ERR_INVALID_ARG),           # not a multiple of 64
+    (mqd(split=-64), pa.ERR_INVALID_ARG),
 ])
 def test_multi_query_rejects_bad_descriptor(desc, code):
     assert _mq(desc) == code
@@ -283,6 +308,11 @@ def test_multi_query_rejects_bad_pointers_and_scale():
     assert _mq(mqd(), out=FAKE + 8) == pa.ERR_INVALID_ARG
     assert _mq(mqd(), qs=FAKE + 2) == pa.ERR_INVALID_ARG
     assert _mq(mqd(), scale=float("nan")) == pa.ERR_INVALID_ARG
+    d = mqd(mb=128, maxctx=2000)
+    n = ctypes.c_size_t(0)
+    pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+    assert _mq(d, ws_bytes=n.value - 1) == pa.ERR_WORKSPACE
+    assert _mq(d, ws=None, ws_bytes=n.value) == pa.ERR_INVALID_ARG
 
 
 def test_multi_query_with_nothing_to_do_launches_nothing():

@@ -46,9 +46,11 @@ def assert_close(got, ref, out_dtype, what):
     return float(err.max()) if err.size else 0.0
 
 
-def gpu_mq(pa, q, kc, vc, tables, ctx, qs, scale, out_dtype=None):
+def gpu_mq(pa, q, kc, vc, tables, ctx, qs, scale, out_dtype=None, split=0):
     out = pa.paged_attn_multi_query(dev(q), dev(kc), dev(vc), dev(tables), dev(ctx), dev(qs), scale,
-                                    max_query_len=int(np.diff(qs).max()), out_dtype=out_dtype)
+                                    max_query_len=int(np.diff(qs).max()),
+                                    max_context_len=int(ctx.max()), out_dtype=out_dtype,
+                                    split_tokens=split)
     torch.cuda.synchronize()
     return di.from_torch(out)
 
@@ -149,3 +151,37 @@ def test_repeat_is_bit_identical(pa):
     a = gpu_mq(pa, q, kc, vc, tables, ctx, qs, 0.09)
     b = gpu_mq(pa, q, kc, vc, tables, ctx, qs, 0.09)
     assert a.tobytes() == b.tobytes()
+
+
+@pytest.mark.parametrize("split", [0, 64, 128, 512, 4096])
+def test_kv_split_sizes_agree_with_oracle(pa, split):
+    # long contexts with short and long query runs: many tiles span several
+    # splits, some rows see none of a split's keys
+    rng = np.random.default_rng(620)
+    qlens, ctx = [1, 4, 20, 64, 3], [3000, 1500, 700, 2100, 64]
+    q, kc, vc, tables, ctx, qs = ragged_case(rng, np.float32, qlens, ctx, 8, 2, 64, 16)
+    ref = oracle.paged_attn_multi_query(q, kc, vc, tables, ctx, qs, 0.125)
+    got = gpu_mq(pa, q, kc, vc, tables, ctx, qs, 0.125, split=split)
+    assert_close(got, ref, np.float32, f"split {split}")
+
+
+def test_split_workspace_reused_stays_zeroed(pa):
+    rng = np.random.default_rng(621)
+    q, kc, vc, tables, ctx, qs = ragged_case(rng, np.float16, [4, 4, 9], [900, 2000, 40], 16, 4, 128, 16)
+    ref = oracle.paged_attn_multi_query(q, kc, vc, tables, ctx, qs, 0.09)
+    args = [dev(q), dev(kc), dev(vc), dev(tables), dev(ctx), dev(qs)]
+    sizes = {}
+    for split in (64, 256, 0):
+        d = pa.multi_query_desc(args[0], args[1], args[3], 3, 9, int(ctx.max()), split)
+        sizes[split] = pa.multi_query_workspace_bytes(d)
+    assert all(v > 0 for v in sizes.values())
+    ws = pa.new_workspace(max(sizes.values()), "cuda:0")
+    tiles = 3 * 4 * ((9 * 4 + 15) // 16)
+    for rep in range(2):
+        for split in (64, 256, 0):
+            out = pa.paged_attn_multi_query(*args, 0.09, max_query_len=9, max_context_len=int(ctx.max()),
+                                            workspace=ws, split_tokens=split)
+            torch.cuda.synchronize()
+            assert_close(di.from_torch(out), ref, np.float16, f"split {split} rep {rep}")
+            counters = ws[: tiles * 4].view(torch.int32).cpu().numpy()
+            assert (counters == 0).all()
