@@ -109,6 +109,8 @@ def parse_args(argv=None):
                          "step (0 skips the rotary measurements)")
     ap.add_argument("--no-multi-query", action="store_true",
                     help="skip the multi-query (speculative verify / chunked prefill) timings")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the continuous-batching serving run")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (default: the step is also captured in a "
                          "HIP graph and replayed, and value uses the replays)")
@@ -355,6 +357,114 @@ def multi_query_measurements(args, cfg, lay, layers, device, stream):
                             "us_per_call": round(prefill_us, 3), "flops_per_call": flops,
                             "tflops": round(tflops, 2),
                             "frac_of_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS["bf16"], 4)},
+    }
+
+
+def serving_measurements(cfg, device, stream, trace_name: str = "serving"):
+    """A continuous-batching run of the attention path, one layer.
+
+    The native scheduler turns a seeded request trace into steps; each step
+    uploads its positions, slots, tables, context lengths and query starts
+    (pinned host buffers, asynchronous copies), then runs the fused rotary +
+    cache write over the step's new tokens and the multi-query kernel over
+    all of them (prefill chunks and decode tokens in one launch), or the
+    decode kernel when every sequence has one new token.  q/k/v of
+    the new tokens are synthetic (no model).  Reported: attention-path GPU
+    time per step (events around the two launches) and new tokens per
+    second, over all steps and over the decode-only steps.
+    """
+    import paged_attention_decode_photon_amd as pa
+    import torch
+    from paged_attention_decode_photon_amd.sched import Scheduler
+
+    tc = di.TRACES[trace_name]
+    trace = di.make_request_trace(tc)
+    hq, hkv, d, bs = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, tc.block_size
+    rng = np.random.default_rng(cfg.seed + 3000)
+    dt = cfg.np_dtype
+    kc = di.to_torch(di.cast(rng.standard_normal((tc.num_blocks, hkv, bs, d)), dt)).to(device)
+    vc = torch.empty_like(kc).copy_(kc)
+    mt = tc.max_tokens_per_step
+    q = di.to_torch(di.cast(rng.standard_normal((mt, hq, d)), dt)).to(device)
+    k = di.to_torch(di.cast(rng.standard_normal((mt, hkv, d)), dt)).to(device)
+    v = torch.empty_like(k).copy_(k)
+    qr, out = torch.empty_like(q), torch.empty_like(q)
+    ms, mb = tc.max_seqs, tc.max_blocks_per_seq
+    host = {"pos": torch.zeros(mt, dtype=torch.int32).pin_memory(),
+            "slot": torch.zeros(mt, dtype=torch.int32).pin_memory(),
+            "tables": torch.zeros(ms * mb, dtype=torch.int32).pin_memory(),
+            "ctx": torch.zeros(ms, dtype=torch.int32).pin_memory(),
+            "qs": torch.zeros(ms + 1, dtype=torch.int32).pin_memory()}
+    devb = {n: torch.empty_like(t, device=device) for n, t in host.items()}
+    ws = pa.new_workspace(1 << 20, device)
+    # decode workspace for the largest decode-only step this trace allows
+    dd = pa.decode_desc(q[:ms], kc, torch.empty((ms, mb), dtype=torch.int32), mb * bs)
+    dec_ws = pa.new_workspace(pa.workspace_bytes(dd), device)
+    sched = Scheduler(**tc.sched_config())
+
+    def event():
+        return torch.cuda.Event(enable_timing=True)
+
+    records = []
+    i, done, step = 0, 0, 0
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    while done < len(trace):
+        while i < len(trace) and trace[i][0] <= step:
+            sched.add_request(*trace[i][1:])
+            i += 1
+        o = sched.schedule()
+        t, b = len(o["slot_mapping"]), len(o["request_ids"])
+        if t:
+            host["pos"][:t].numpy()[:] = o["positions"]
+            host["slot"][:t].numpy()[:] = o["slot_mapping"]
+            host["tables"][:b * mb].numpy()[:] = o["block_tables"].ravel()
+            host["ctx"][:b].numpy()[:] = o["context_lens"]
+            host["qs"][:b + 1].numpy()[:] = o["query_start"]
+            for n in host:
+                devb[n].copy_(host[n], non_blocking=True)
+            maxq = int(np.diff(o["query_start"]).max())
+            maxc = int(o["context_lens"].max())
+            tables = devb["tables"][:b * mb].view(b, mb)
+            desc = pa.multi_query_desc(q[:t], kc, tables, b, maxq, maxc)
+            need = pa.multi_query_workspace_bytes(desc)
+            if need > ws.numel():
+                ws = pa.new_workspace(need, device)
+            e0, e1 = event(), event()
+            e0.record(stream)
+            pa.rope_kv_cache_write(q[:t], k[:t], v[:t], devb["pos"][:t], devb["slot"][:t], kc, vc,
+                                   cfg.rope_base, q_out=qr[:t])
+            if maxq == 1:  # decode-only step: the balanced decode kernel
+                pa.paged_attn_decode(qr[:t], kc, vc, tables, devb["ctx"][:b], cfg.scale,
+                                     max_context_len=maxc, out=out[:t], workspace=dec_ws)
+            else:
+                pa.paged_attn_multi_query(qr[:t], kc, vc, tables, devb["ctx"][:b],
+                                          devb["qs"][:b + 1], cfg.scale, max_query_len=maxq,
+                                          max_context_len=maxc, out=out[:t], workspace=ws)
+            e1.record(stream)
+            records.append((e0, e1, t, b, maxq))
+            # the host buffers are rewritten next step: wait for this step's copies
+            e1.synchronize()
+        done += len(sched.update())
+        step += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_us = [a.elapsed_time(z) * 1e3 for a, z, _, _, _ in records]
+    toks = sum(r[2] for r in records)
+    dec = [(us, r[2]) for us, r in zip(gpu_us, records) if r[4] == 1]
+    return {
+        "trace": trace_name, "dtype": cfg.dtype, "requests": len(trace), "steps": step,
+        "kernels": "rope_kv_cache_write, then paged_decode_kernel (decode-only steps) or "
+                   "paged_mq_kernel (steps with prompt chunks), one layer",
+        "new_tokens": toks,
+        "gpu_us_per_step_mean": round(statistics.fmean(gpu_us), 2),
+        "tokens_per_s_gpu": round(toks / (sum(gpu_us) * 1e-6), 1),
+        "decode_only_steps": len(dec),
+        "decode_only_us_per_step_mean": round(statistics.fmean(u for u, _ in dec), 2) if dec else None,
+        "decode_only_tokens_per_s_gpu": round(sum(n for _, n in dec) / (sum(u for u, _ in dec) * 1e-6), 1)
+        if dec else None,
+        "wall_s": round(wall, 3),
+        "note": "wall time includes scheduling, uploads and a wait per step (the host buffers are reused)",
     }
 
 
@@ -630,6 +740,8 @@ def main(argv=None) -> int:
     if mq is not None:
         result["multi_query"] = mq
     result["scheduler"] = scheduler_measurements()
+    if not args.no_serving:
+        result["serving"] = serving_measurements(cfg, device, stream)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, lay, host_layers, args.cpu_seconds)
     print(json.dumps(result), flush=True)
