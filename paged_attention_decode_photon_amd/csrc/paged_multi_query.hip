@@ -63,6 +63,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(float *rec, int float
 }
 constexpr int kRawWord3 = 0x00020000;
 constexpr int kTile = 16;  // query rows per tile, tokens per KV block
+// Calls whose longest query run spans at least this many tiles use the wide
+// kernel (four tiles per workgroup sharing each K/V block through LDS).
+#ifndef PHOTON_MQ_WIDE_TILES
+#define PHOTON_MQ_WIDE_TILES 4
+#endif
+constexpr int kWideTiles = PHOTON_MQ_WIDE_TILES;
 
 __device__ __forceinline__ void wave_sync()
 {
@@ -112,6 +118,109 @@ __device__ __forceinline__ f32x4 mfma16(const u32x2 &a, const u32x2 &b, f32x4 c)
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                          __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
+
+// The online-softmax state of one wave's 16 query rows (lane l: row l % 16)
+// and the three per-block steps both kernels share.
+template <typename T, int D>
+struct TileState {
+    static constexpr int EB = sizeof(T);
+    static constexpr int QD = D / 4;           // head-dimension elements per lane
+    static constexpr int NW = QD * EB / 4;     // dwords of them
+    static constexpr int MT = D / 16;          // 16-wide output column tiles
+    static constexpr int VS = kTile + 4;       // LDS row stride of a transposed V tile
+
+    float m_run = -INFINITY, l_lane = 0.0f;
+    f32x4 o_acc[MT];
+
+    __device__ TileState()
+    {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            o_acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    // S^T = K Q^T over one 16-token block: lane l gets tokens 4 (l/16) + i of row l % 16.
+    __device__ static f32x4 scores(const uint32_t (&kw)[NW], const uint32_t (&qw)[NW])
+    {
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (EB == 4) {
+#pragma unroll
+            for (int k = 0; k < QD; ++k)
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[k]),
+                                                         __uint_as_float(qw[k]), s, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int k = 0; k < QD / 4; ++k)
+                s = mfma16<T>(u32x2{kw[2 * k], kw[2 * k + 1]}, u32x2{qw[2 * k], qw[2 * k + 1]}, s);
+        }
+        return s;
+    }
+
+    // One softmax update over NB blocks n0 .. n0 + NB - 1 (those with
+    // live[bi]): scores in log2 units, tokens past my_pos (or any token of a
+    // padding row) masked; p receives the weights.  One maximum reduction
+    // and one rescale of the accumulators per call, however many blocks.
+    template <int NB>
+    __device__ void update(const f32x4 (&s)[NB], const bool (&live)[NB], int n0, bool row_ok,
+                           int my_pos, float qscale, int gq, float (&p)[NB][4])
+    {
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = (n0 + bi) * kTile + 4 * gq + i;
+                p[bi][i] = (live[bi] && row_ok && t <= my_pos) ? s[bi][i] * qscale : -INFINITY;
+                bmax = fmaxf(bmax, p[bi][i]);
+            }
+        bmax = allreduce_pair<16, OpMax>(bmax);
+        bmax = allreduce_pair<32, OpMax>(bmax);
+        const float m_new = fmaxf(m_run, bmax);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        float psum = 0.0f;
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[bi][i] = __builtin_amdgcn_exp2f(p[bi][i] - m_use);
+                psum += p[bi][i];
+            }
+        l_lane = l_lane * alpha + psum;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            o_acc[t] *= alpha;
+    }
+
+    // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS.
+    __device__ void pv(const T *vt, int lr, int gq, const float (&p)[4])
+    {
+        if constexpr (EB == 4) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const f32x4 va = *reinterpret_cast<const f32x4 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], p[i], o_acc[t], 0, 0, 0);
+            }
+        } else {
+            const u32x2 p_hi = round4<T>(p);
+            float hi[4], lo[4];
+            widen4<T>(p_hi, hi);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lo[i] = p[i] - hi[i];
+            const u32x2 p_lo = round4<T>(lo);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const u32x2 va = *reinterpret_cast<const u32x2 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
+                o_acc[t] = mfma16<T>(va, p_hi, o_acc[t]);
+                o_acc[t] = mfma16<T>(va, p_lo, o_acc[t]);
+            }
+        }
+    }
+};
 
 // Workgroup-level running max and exponential sum of tile row r, from the
 // four waves' statistics (the same values every lane forms in the merge).
@@ -200,11 +309,8 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         }
     }
 
-    float m_run = -INFINITY, l_lane = 0.0f;
-    f32x4 o_acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-        o_acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    using TS = TileState<T, D>;
+    TS st;
     T *vt = reinterpret_cast<T *>(smem + wave * VT_BYTES);
     const size_t tile_elems = (size_t)kTile * D;
 
@@ -232,19 +338,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
 
     // Scores, softmax update and P.V of block n from its loaded K and V.
     auto compute_block = [&](int n, const uint32_t (&kw)[NW], const uint32_t (&vw)[NW]) {
-        // S^T = K Q^T for this block.
-        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (EB == 4) {
-#pragma unroll
-            for (int k = 0; k < QD; ++k)
-                s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[k]), __uint_as_float(qw[k]),
-                                                         s, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int k = 0; k < QD / 4; ++k)
-                s = mfma16<T>(u32x2{kw[2 * k], kw[2 * k + 1]}, u32x2{qw[2 * k], qw[2 * k + 1]}, s);
-        }
-
+        const f32x4 sc = TS::scores(kw, qw);
         // V^T into LDS: element (d, token lr) of this lane's quarter.
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -258,59 +352,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
                 vt[(gq * QD + 2 * w + 1) * VS + lr] = pair[1];
             }
         }
-
-        // Scores in log2 units; tokens past this row's position are masked.
-        float p[4];
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = n * kTile + 4 * gq + i;
-            p[i] = (row_ok && t <= my_pos) ? s[i] * a.qscale : -INFINITY;
-            bmax = fmaxf(bmax, p[i]);
-        }
-        bmax = allreduce_pair<16, OpMax>(bmax);
-        bmax = allreduce_pair<32, OpMax>(bmax);
-        const float m_new = fmaxf(m_run, bmax);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        float psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(p[i] - m_use);
-            psum += p[i];
-        }
-        l_lane = l_lane * alpha + psum;
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-            o_acc[t] *= alpha;
-
+        float p[1][4];
+        const f32x4 sv[1] = {sc};
+        const bool live[1] = {true};
+        st.template update<1>(sv, live, n, row_ok, my_pos, a.qscale, gq, p);
         wave_sync();  // the transposed V tile is complete
-
-        // O^T += V^T P^T.
-        if constexpr (EB == 4) {
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const f32x4 va = *reinterpret_cast<const f32x4 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], p[i], o_acc[t], 0, 0, 0);
-            }
-        } else {
-            const u32x2 p_hi = round4<T>(p);
-            float hi[4], lo[4];
-            widen4<T>(p_hi, hi);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                lo[i] = p[i] - hi[i];
-            const u32x2 p_lo = round4<T>(lo);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const u32x2 va = *reinterpret_cast<const u32x2 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
-                o_acc[t] = mfma16<T>(va, p_hi, o_acc[t]);
-                o_acc[t] = mfma16<T>(va, p_lo, o_acc[t]);
-            }
-        }
+        st.pv(vt, lr, gq, p[0]);
         wave_sync();  // reads of the V tile are done before the next block overwrites it
     };
 
@@ -328,8 +375,9 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     }
 
     // Merge the four waves' partial states of each row.
-    float l_row = allreduce_pair<16, OpSum>(l_lane);
+    float l_row = allreduce_pair<16, OpSum>(st.l_lane);
     l_row = allreduce_pair<32, OpSum>(l_row);
+    const float m_run = st.m_run;
     if (gq == 0) {
         stat_m[wave][lr] = m_run;
         stat_l[wave][lr] = l_row;
@@ -347,7 +395,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            ob[lr * D + 16 * t + 4 * gq + i] = o_acc[t][i] * f;
+            ob[lr * D + 16 * t + 4 * gq + i] = st.o_acc[t][i] * f;
     __syncthreads();
 
     // Sum the four partial rows: thread -> (row, D/16 columns).
@@ -445,12 +493,288 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         __hip_atomic_store(&a.ws_count[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wide variant for long query runs (chunked prefill): a workgroup takes four
+// consecutive tiles of one (sequence, KV head), one wave per tile, and
+// walks the KV blocks of its split once: each 16-token block of K and V is
+// loaded by the whole workgroup into LDS (K row-major, V transposed;
+// double-buffered, the next block's loads in flight during the current
+// block's math) and read by all four waves, so K/V are fetched once per 64
+// query rows instead of once per 16.  A wave skips blocks wholly past its
+// rows' positions.  Each wave finishes its own tile: directly with one
+// split, else through the per-tile records and arrival counter.
+template <typename T, typename O, int D, int G>
+__global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQueryArgs a)
+{
+    using TS = TileState<T, D>;
+    constexpr int EB = sizeof(T);
+    constexpr int QD = TS::QD, NW = TS::NW, MT = TS::MT, VS = TS::VS;
+    constexpr int NL = QD * EB / 16;           // 16-byte loads per lane per row part
+    constexpr int EC = 16 / EB;                // elements per 16-byte chunk
+    constexpr int CH = D / EC;                 // chunks per row
+    constexpr int KS = D + EC;                 // LDS row stride of K (one chunk of padding)
+    constexpr int NCH = 2 * kTile * CH;        // chunks of one K block plus one V block
+    constexpr int PER = (NCH + kMqWaves * 64 - 1) / (kMqWaves * 64);
+    // KV blocks per step: as many as keep the whole workgroup at 16 bytes of
+    // K/V per thread per step (one round trip to memory per step).
+    constexpr int NB = PER >= 4 ? 1 : 4 / PER;
+    __shared__ __attribute__((aligned(16))) T kl[2][NB * kTile * KS];
+    __shared__ __attribute__((aligned(16))) T vtl[2][NB * D * VS];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gq = lane >> 4;
+    const int lr = lane & 15;
+    const int hkv = a.num_kv_heads;
+    const int b = blockIdx.y / hkv;
+    const int g = blockIdx.y - b * hkv;
+    const int q0 = a.query_start[b];
+    const int nq = a.query_start[b + 1] - q0;
+    const int rows = nq * G;
+    const int tile0 = blockIdx.x * kMqWaves;
+    if (tile0 * kTile >= rows)
+        return;  // the whole workgroup leaves together
+    const int ctx = a.context_lens[b];
+    const int first_pos = ctx - nq;
+    const int wg_last_row = min((tile0 + kMqWaves) * kTile - 1, rows - 1);
+    const int scan_end = first_pos + wg_last_row / G + 1;
+    const int nblk = (scan_end + kTile - 1) / kTile;
+    const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
+    const int z = blockIdx.z;
+    if (z >= nsplit)
+        return;
+    const int n_begin = z * a.split_blocks;
+    const int n_end = min(nblk, n_begin + a.split_blocks);
+
+    const int tile = tile0 + wave;
+    const bool has_rows = tile * kTile < rows;   // wave-uniform
+    const int r = tile * kTile + lr;
+    const bool row_ok = r < rows;
+    const int my_pos = first_pos + r / G;
+    const int wave_last_pos = first_pos + min(tile * kTile + kTile - 1, rows - 1) / G;
+    const int hq = hkv * G;
+
+    uint32_t qw[NW];
+    {
+        const int cr = row_ok ? r : rows - 1;
+        const int cj = cr / G, ch = cr - (cr / G) * G;
+        const T *qrow = (const T *)a.q + ((size_t)(q0 + cj) * hq + (size_t)g * G + ch) * D + gq * QD;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            u32x4 v = reinterpret_cast<const u32x4 *>(qrow)[i];
+            if (!row_ok)
+                v = u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                qw[4 * i + k] = v[k];
+        }
+    }
+
+    // Whole-workgroup loads of the NB blocks starting at n0: chunk c of
+    // this thread covers K (first half of the chunks) or V, row c / CH,
+    // 16-byte column c % CH; blocks at or past n_end read as zero rows.
+    const size_t tile_elems = (size_t)kTile * D;
+    auto gload = [&](int n0, u32x4 (&regs)[NB][PER]) {
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi) {
+            const int n = n0 + bi;
+            const bool live = n < n_end;
+            const int blk = __builtin_amdgcn_readfirstlane(
+                a.block_tables[(size_t)b * a.max_blocks + (live ? n : n0)]);
+            const int valid = live ? min(kTile, scan_end - n * kTile) : 0;
+            const size_t base = ((size_t)blk * hkv + g) * tile_elems;
+            const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((const T *)a.k_cache + base), (short)0, valid * D * EB, kRawWord3);
+            const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((const T *)a.v_cache + base), (short)0, valid * D * EB, kRawWord3);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int c = threadIdx.x + i * kMqWaves * 64;
+                const int rc = c % (kTile * CH);
+                regs[bi][i] = c < kTile * CH ? __builtin_amdgcn_raw_buffer_load_b128(krs, rc * 16, 0, 0)
+                                             : __builtin_amdgcn_raw_buffer_load_b128(vrs, rc * 16, 0, 0);
+            }
+        }
+    };
+    auto lstore = [&](int buf, const u32x4 (&regs)[NB][PER]) {
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi) {
+            T *kb = &kl[buf][bi * kTile * KS];
+            T *vb = &vtl[buf][bi * D * VS];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int c = threadIdx.x + i * kMqWaves * 64;
+                if (c >= NCH)
+                    break;
+                const int rc = c % (kTile * CH);
+                const int row = rc / CH, col = rc % CH;
+                if (c < kTile * CH) {
+                    *reinterpret_cast<u32x4 *>(&kb[row * KS + col * EC]) = regs[bi][i];
+                } else {
+                    const u32x4 w = regs[bi][i];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t word = w[k];
+                        if constexpr (EB == 4) {
+                            vb[(col * EC + k) * VS + row] = __builtin_bit_cast(T, word);
+                        } else {
+                            typedef T t2 __attribute__((ext_vector_type(2)));
+                            const t2 pair = __builtin_bit_cast(t2, word);
+                            vb[(col * EC + 2 * k) * VS + row] = pair[0];
+                            vb[(col * EC + 2 * k + 1) * VS + row] = pair[1];
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    TS st;
+    u32x4 regs[NB][PER];
+    if (n_begin < n_end) {
+        gload(n_begin, regs);
+        lstore(0, regs);
+    }
+    __syncthreads();
+    for (int n0 = n_begin; n0 < n_end; n0 += NB) {
+        const int buf = ((n0 - n_begin) / NB) & 1;
+        const bool more = n0 + NB < n_end;
+        if (more)
+            gload(n0 + NB, regs);  // in flight while these blocks are used
+        if (has_rows && n0 * kTile <= wave_last_pos) {
+            // scores of the step's blocks, one softmax update, then P.V
+            f32x4 sc[NB];
+            bool live[NB];
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi) {
+                const int n = n0 + bi;
+                live[bi] = n < n_end && n * kTile <= wave_last_pos;  // wave-uniform
+                sc[bi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (live[bi]) {
+                    uint32_t kw[NW];
+                    const T *krow = &kl[buf][(bi * kTile + lr) * KS + gq * QD];
+#pragma unroll
+                    for (int i = 0; i < NL; ++i) {
+                        const u32x4 v = reinterpret_cast<const u32x4 *>(krow)[i];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            kw[4 * i + k] = v[k];
+                    }
+                    sc[bi] = TS::scores(kw, qw);
+                }
+            }
+            float p[NB][4];
+            st.template update<NB>(sc, live, n0, row_ok, my_pos, a.qscale, gq, p);
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi)
+                if (live[bi])
+                    st.pv(&vtl[buf][bi * D * VS], lr, gq, p[bi]);
+        }
+        if (more)
+            lstore(buf ^ 1, regs);
+        __syncthreads();  // the next buffer is filled; this one is no longer read
+    }
+    if (!has_rows)
+        return;
+
+    // This wave's tile: lane holds O^T[16 t + 4 gq + i][row lr].
+    float l_row = allreduce_pair<16, OpSum>(st.l_lane);
+    l_row = allreduce_pair<32, OpSum>(l_row);
+    const int oj = r / G, oh = r - (r / G) * G;
+    O *dst = (O *)a.out + ((size_t)(q0 + oj) * hq + (size_t)g * G + oh) * D + 4 * gq;
+    if (nsplit == 1) {
+        if (row_ok) {
+            const float inv = 1.0f / l_row;
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dst[16 * t + i] = Elem<O>::from_float(st.o_acc[t][i] * inv);
+        }
+        return;
+    }
+    constexpr int REC = kTile * D + 2 * kTile;
+    const size_t tile_id = (size_t)blockIdx.y * a.max_tiles + tile;
+    {
+        const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a.ws_rec + (tile_id * gridDim.z + z) * REC, REC);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(st.o_acc[t][0]), __float_as_uint(st.o_acc[t][1]),
+                      __float_as_uint(st.o_acc[t][2]), __float_as_uint(st.o_acc[t][3])},
+                rs, (lr * D + 16 * t + 4 * gq) * 4, 0, kSc1);
+        if (gq == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st.m_run), rs, (kTile * D + lr) * 4,
+                                                  0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_row), rs,
+                                                  (kTile * D + kTile + lr) * 4, 0, kSc1);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the whole wave's record is stored
+    int arrived = 0;
+    if (lane == 0)
+        arrived = __hip_atomic_fetch_add(&a.ws_count[tile_id], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) + 1;
+    arrived = __builtin_amdgcn_readfirstlane(arrived);
+    if (arrived != nsplit)
+        return;
+    asm volatile("" ::: "memory");
+    float mz_max = -INFINITY;
+    for (int zz = 0; zz < nsplit; ++zz) {
+        const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a.ws_rec + (tile_id * gridDim.z + zz) * REC, REC);
+        mz_max = fmaxf(mz_max, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                   rs, (kTile * D + lr) * 4, 0, kSc1)));
+    }
+    float lsum = 0.0f;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int zz = 0; zz < nsplit; ++zz) {
+        const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a.ws_rec + (tile_id * gridDim.z + zz) * REC, REC);
+        const float mz = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rs, (kTile * D + lr) * 4, 0, kSc1));
+        const float lz = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rs, (kTile * D + kTile + lr) * 4, 0, kSc1));
+        const float wz = mz == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mz - mz_max);
+        lsum = __builtin_fmaf(wz, lz, lsum);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const u32x4 oz = __builtin_amdgcn_raw_buffer_load_b128(rs, (lr * D + 16 * t + 4 * gq) * 4,
+                                                                  0, kSc1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[t][i] = __builtin_fmaf(wz, __uint_as_float(oz[i]), acc[t][i]);
+        }
+    }
+    if (row_ok) {
+        const float inv = 1.0f / lsum;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dst[16 * t + i] = Elem<O>::from_float(acc[t][i] * inv);
+    }
+    if (lane == 0)
+        __hip_atomic_store(&a.ws_count[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename T, typename O, int D>
 hipError_t launch_mq_group(const MultiQueryArgs &a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.num_seqs * a.num_kv_heads),
-                    (unsigned)a.num_splits);
     const dim3 block(kMqWaves * 64);
+    const unsigned yz = (unsigned)(a.num_seqs * a.num_kv_heads);
+    if (a.max_tiles >= kWideTiles) {
+        const dim3 grid((unsigned)((a.max_tiles + kMqWaves - 1) / kMqWaves), yz, (unsigned)a.num_splits);
+        switch (a.group) {
+        case 1: hipLaunchKernelGGL((paged_mq_wide_kernel<T, O, D, 1>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((paged_mq_wide_kernel<T, O, D, 2>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((paged_mq_wide_kernel<T, O, D, 4>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((paged_mq_wide_kernel<T, O, D, 8>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)a.max_tiles, yz, (unsigned)a.num_splits);
     switch (a.group) {
     case 1: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 1>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 2>), grid, block, 0, stream, a); break;

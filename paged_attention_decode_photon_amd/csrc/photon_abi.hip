@@ -194,6 +194,9 @@ constexpr int64_t kMqTargetGroups = 1024;
 // ... but no split shorter than 32 blocks: each wave then runs at least four
 // blocks, two at a time (measured best for 4-token verification at batch 16).
 constexpr int64_t kMqMinSplitBlocks = 32;
+// ... and none longer than 64 blocks (1024 tokens): a long prompt chunk at a
+// long context is then spread over several workgroups.
+constexpr int64_t kMqMaxSplitBlocks = 64;
 
 photon_status plan_multi_query(const photon_multi_query_desc *d, MqPlan *plan)
 {
@@ -244,6 +247,7 @@ photon_status plan_multi_query(const photon_multi_query_desc *d, MqPlan *plan)
         sb = want > 1 ? (max_nblk + want - 1) / want : max_nblk;
         sb = (sb + 7) / 8 * 8;  // whole steps: four waves, two blocks each
         sb = sb < kMqMinSplitBlocks ? kMqMinSplitBlocks : sb;
+        sb = sb > kMqMaxSplitBlocks ? kMqMaxSplitBlocks : sb;
     }
     const int64_t splits = max_nblk > sb ? (max_nblk + sb - 1) / sb : 1;
     if (splits > 65535)
