@@ -407,3 +407,46 @@ def test_fused_step_graph_replays_match_eager(pa):
         graph.replay()
         torch.cuda.synchronize()
         assert host(out).tobytes() == host(eager).tobytes(), f"replay {rep} differs"
+
+
+# ---------------------------------------------------------------- limits
+
+def test_decode_at_the_largest_batch(pa):
+    # 2048 sequences (the most a call takes), ragged short contexts with
+    # empty ones mixed in, through the fused step and the plain decode
+    rng = np.random.default_rng(40)
+    ctx = rng.integers(0, 80, 2048).astype(np.int32)
+    ctx[::97] = 0
+    q, kc, vc, tables, ctx = random_case(rng, np.float16, 0, 16, 8, 64, ctx_list=ctx)
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    got = gpu_decode(pa, q, kc, vc, tables, ctx, 0.125)
+    assert_close(got, ref, np.float16, "B=2048")
+    assert (di.as_float64(got[ctx == 0]) == 0).all()
+
+
+def test_context_filling_the_whole_table(pa):
+    # every sequence uses every entry of its table row, the last block full
+    rng = np.random.default_rng(41)
+    ctx = [16 * 40] * 3 + [16 * 40 - 1]
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 0, 32, 8, 64, ctx_list=ctx)
+    assert tables.shape[1] * 16 == int(ctx.max())
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    for part in (0, 32, 640):
+        got = gpu_decode(pa, q, kc, vc, tables, ctx, 0.125, max_ctx=tables.shape[1] * 16, part=part)
+        assert_close(got, ref, np.float32, f"full tables, partition {part}")
+
+
+def test_cache_write_many_tokens(pa):
+    # 65536 tokens into a pool of 8192 blocks: bit-exact over the whole pool
+    rng = np.random.default_rng(42)
+    nb, hkv, d, t = 8192, 8, 64, 65536
+    kc = rng.standard_normal((nb, hkv, 16, d)).astype(np.float16)
+    vc = rng.standard_normal((nb, hkv, 16, d)).astype(np.float16)
+    k = rng.standard_normal((t, hkv, d)).astype(np.float16)
+    v = rng.standard_normal((t, hkv, d)).astype(np.float16)
+    slots = di.random_injective_slots(nb, 16, t, rng, pad_fraction=0.1)
+    ek, ev = oracle.kv_cache_write(k, v, slots, kc, vc)
+    gk, gv = dev(kc), dev(vc)
+    pa.kv_cache_write(dev(k), dev(v), dev(slots), gk, gv)
+    torch.cuda.synchronize()
+    assert host(gk).tobytes() == ek.tobytes() and host(gv).tobytes() == ev.tobytes()
