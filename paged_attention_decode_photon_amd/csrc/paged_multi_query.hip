@@ -158,11 +158,20 @@ struct TileState {
 
     // One softmax update over NB blocks n0 .. n0 + NB - 1 (those with
     // live[bi]): scores in log2 units, tokens past my_pos (or any token of a
-    // padding row) masked; p receives the weights.  One maximum reduction
-    // and one rescale of the accumulators per call, however many blocks.
+    // padding row) masked, unless `unmasked` says every token of the blocks
+    // lies at or before every row's position (wave-uniform); p receives the
+    // weights.  One maximum reduction per call, however many blocks.
+    //
+    // The accumulators are rescaled lazily: the reference maximum m_run only
+    // moves (and o, l are rescaled) when some row of the wave sees a score
+    // more than kSlack above it; otherwise the weights are formed against
+    // the old reference and stay below 2^kSlack.  o and l always share one
+    // reference, so the normalised result is the same up to rounding.
+    static constexpr float kSlack = 8.0f;
+
     template <int NB>
-    __device__ void update(const f32x4 (&s)[NB], const bool (&live)[NB], int n0, bool row_ok,
-                           int my_pos, float qscale, int gq, float (&p)[NB][4])
+    __device__ void update(const f32x4 (&s)[NB], const bool (&live)[NB], bool unmasked, int n0,
+                           bool row_ok, int my_pos, float qscale, int gq, float (&p)[NB][4])
     {
         float bmax = -INFINITY;
 #pragma unroll
@@ -170,15 +179,23 @@ struct TileState {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = (n0 + bi) * kTile + 4 * gq + i;
-                p[bi][i] = (live[bi] && row_ok && t <= my_pos) ? s[bi][i] * qscale : -INFINITY;
+                const float v = s[bi][i] * qscale;
+                p[bi][i] = (unmasked || (live[bi] && row_ok && t <= my_pos)) ? v : -INFINITY;
                 bmax = fmaxf(bmax, p[bi][i]);
             }
         bmax = allreduce_pair<16, OpMax>(bmax);
         bmax = allreduce_pair<32, OpMax>(bmax);
-        const float m_new = fmaxf(m_run, bmax);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(bmax > m_run + kSlack) != 0) {
+            const float m_new = fmaxf(m_run, bmax);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            m_run = m_new;
+            l_lane *= alpha;
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                o_acc[t] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
         float psum = 0.0f;
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi)
@@ -187,10 +204,7 @@ struct TileState {
                 p[bi][i] = __builtin_amdgcn_exp2f(p[bi][i] - m_use);
                 psum += p[bi][i];
             }
-        l_lane = l_lane * alpha + psum;
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-            o_acc[t] *= alpha;
+        l_lane += psum;
     }
 
     // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS.
@@ -312,6 +326,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     using TS = TileState<T, D>;
     TS st;
     T *vt = reinterpret_cast<T *>(smem + wave * VT_BYTES);
+    const int tile_first_pos = first_pos + (tile * kTile) / G;  // the tile's earliest row
     const size_t tile_elems = (size_t)kTile * D;
 
     // Issue the K and V loads of block n (zero rows when !live).
@@ -355,7 +370,8 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         float p[1][4];
         const f32x4 sv[1] = {sc};
         const bool live[1] = {true};
-        st.template update<1>(sv, live, n, row_ok, my_pos, a.qscale, gq, p);
+        st.template update<1>(sv, live, (n + 1) * kTile - 1 <= tile_first_pos, n, row_ok, my_pos,
+                              a.qscale, gq, p);
         wave_sync();  // the transposed V tile is complete
         st.pv(vt, lr, gq, p[0]);
         wave_sync();  // reads of the V tile are done before the next block overwrites it
@@ -513,6 +529,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
     constexpr int CH = D / EC;                 // chunks per row
     constexpr int KS = D + EC;                 // LDS row stride of K (one chunk of padding)
     constexpr int NCH = 2 * kTile * CH;        // chunks of one K block plus one V block
+    static_assert((kTile * CH) % 64 == 0, "each wave loads K chunks only or V chunks only");
     constexpr int PER = (NCH + kMqWaves * 64 - 1) / (kMqWaves * 64);
     // KV blocks per step: as many as keep the whole workgroup at 16 bytes of
     // K/V per thread per step (one round trip to memory per step).
@@ -551,6 +568,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
     const bool row_ok = r < rows;
     const int my_pos = first_pos + r / G;
     const int wave_last_pos = first_pos + min(tile * kTile + kTile - 1, rows - 1) / G;
+    const int wave_first_pos = first_pos + (tile * kTile) / G;
     const int hq = hkv * G;
 
     uint32_t qw[NW];
@@ -590,8 +608,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
             for (int i = 0; i < PER; ++i) {
                 const int c = threadIdx.x + i * kMqWaves * 64;
                 const int rc = c % (kTile * CH);
-                regs[bi][i] = c < kTile * CH ? __builtin_amdgcn_raw_buffer_load_b128(krs, rc * 16, 0, 0)
-                                             : __builtin_amdgcn_raw_buffer_load_b128(vrs, rc * 16, 0, 0);
+                // K and V chunks split at a multiple of 64, so a wave loads
+                // only one of them: keep the descriptor choice scalar.
+                const bool is_k = __builtin_amdgcn_readfirstlane(c < kTile * CH ? 1 : 0) != 0;
+                regs[bi][i] = __builtin_amdgcn_raw_buffer_load_b128(is_k ? krs : vrs, rc * 16, 0, 0);
             }
         }
     };
@@ -607,7 +627,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
                     break;
                 const int rc = c % (kTile * CH);
                 const int row = rc / CH, col = rc % CH;
-                if (c < kTile * CH) {
+                if (__builtin_amdgcn_readfirstlane(c < kTile * CH ? 1 : 0) != 0) {
                     *reinterpret_cast<u32x4 *>(&kb[row * KS + col * EC]) = regs[bi][i];
                 } else {
                     const u32x4 w = regs[bi][i];
@@ -663,7 +683,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
                 }
             }
             float p[NB][4];
-            st.template update<NB>(sc, live, n0, row_ok, my_pos, a.qscale, gq, p);
+            bool all_live = true;
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi)
+                all_live = all_live && live[bi];
+            const bool unmasked = all_live && (n0 + NB) * kTile - 1 <= wave_first_pos;
+            st.template update<NB>(sc, live, unmasked, n0, row_ok, my_pos, a.qscale, gq, p);
 #pragma unroll
             for (int bi = 0; bi < NB; ++bi)
                 if (live[bi])
