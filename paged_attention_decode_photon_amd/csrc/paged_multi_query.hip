@@ -53,6 +53,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short lds_i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMqWaves = 4;
 constexpr int kSc1 = 16;  // cache-policy bits of device-scope record accesses
@@ -117,6 +118,19 @@ __device__ __forceinline__ f32x4 mfma16(const u32x2 &a, const u32x2 &b, f32x4 c)
     else
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                          __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+// Transposing LDS read of 16-bit data (gfx950).  Within each group of 16
+// lanes, lane i returns element i % 4 of the 8 bytes read by lane
+// 4 k + i / 4, for k = 0..3: when lane w of the group points at row w / 4
+// (4 consecutive elements starting at column 4 (w % 4)) of a row-major
+// tile, lane i receives column i of those 4 rows, i.e. one column of the
+// tile across 4 consecutive rows.
+__device__ __forceinline__ u32x2 lds_read_transposed(const void *p)
+{
+    const lds_i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) lds_i16x4 *)p);
+    return __builtin_bit_cast(u32x2, v);
 }
 
 // The online-softmax state of one wave's 16 query rows (lane l: row l % 16)
@@ -205,6 +219,28 @@ struct TileState {
                 psum += p[bi][i];
             }
         l_lane += psum;
+    }
+
+    // O^T += V^T P^T with V row-major in LDS (16 tokens x D, row stride
+    // ks), 16-bit storage only: the A operand (column d = 16 t + lr of
+    // tokens 4 gq .. 4 gq + 3) comes from one transposing read per tile.
+    __device__ void pv_rows(const T *v, int ks, int lr, int gq, const float (&p)[4])
+    {
+        static_assert(EB == 2, "transposing LDS reads are 16-bit");
+        const u32x2 p_hi = round4<T>(p);
+        float hi[4], lo[4];
+        widen4<T>(p_hi, hi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lo[i] = p[i] - hi[i];
+        const u32x2 p_lo = round4<T>(lo);
+        const T *src = &v[(4 * gq + (lr >> 2)) * ks + 4 * (lr & 3)];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const u32x2 va = lds_read_transposed(src + 16 * t);
+            o_acc[t] = mfma16<T>(va, p_hi, o_acc[t]);
+            o_acc[t] = mfma16<T>(va, p_lo, o_acc[t]);
+        }
     }
 
     // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS.
@@ -534,8 +570,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
     // KV blocks per step: as many as keep the whole workgroup at 16 bytes of
     // K/V per thread per step (one round trip to memory per step).
     constexpr int NB = PER >= 4 ? 1 : 4 / PER;
+    // 16-bit V stays row-major (like K) and is read back through the
+    // transposing LDS read; fp32 V is stored transposed.
+    constexpr bool kRowV = EB == 2;
+    constexpr int VBLK = kRowV ? kTile * KS : D * VS;  // LDS elements of one V block
     __shared__ __attribute__((aligned(16))) T kl[2][NB * kTile * KS];
-    __shared__ __attribute__((aligned(16))) T vtl[2][NB * D * VS];
+    __shared__ __attribute__((aligned(16))) T vtl[2][NB * VBLK];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -619,7 +659,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi) {
             T *kb = &kl[buf][bi * kTile * KS];
-            T *vb = &vtl[buf][bi * D * VS];
+            T *vb = &vtl[buf][bi * VBLK];
 #pragma unroll
             for (int i = 0; i < PER; ++i) {
                 const int c = threadIdx.x + i * kMqWaves * 64;
@@ -629,6 +669,8 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
                 const int row = rc / CH, col = rc % CH;
                 if (__builtin_amdgcn_readfirstlane(c < kTile * CH ? 1 : 0) != 0) {
                     *reinterpret_cast<u32x4 *>(&kb[row * KS + col * EC]) = regs[bi][i];
+                } else if constexpr (kRowV) {
+                    *reinterpret_cast<u32x4 *>(&vb[row * KS + col * EC]) = regs[bi][i];
                 } else {
                     const u32x4 w = regs[bi][i];
 #pragma unroll
@@ -691,8 +733,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
             st.template update<NB>(sc, live, unmasked, n0, row_ok, my_pos, a.qscale, gq, p);
 #pragma unroll
             for (int bi = 0; bi < NB; ++bi)
-                if (live[bi])
-                    st.pv(&vtl[buf][bi * D * VS], lr, gq, p[bi]);
+                if (live[bi]) {
+                    if constexpr (kRowV)
+                        st.pv_rows(&vtl[buf][bi * VBLK], KS, lr, gq, p[bi]);
+                    else
+                        st.pv(&vtl[buf][bi * VBLK], lr, gq, p[bi]);
+                }
         }
         if (more)
             lstore(buf ^ 1, regs);
