@@ -108,6 +108,24 @@ __device__ __forceinline__ void widen4(const u32x2 &w, float (&f)[4])
     }
 }
 
+// widen4 written on the packed bits: bfloat16 widens by a shift or a mask
+// of the word it was packed in (so the compiler does not re-round the fp32
+// source); binary16 converts each half.
+template <typename T>
+__device__ __forceinline__ void widen_packed(const u32x2 &w, float (&f)[4])
+{
+    if constexpr (__is_same(T, __bf16)) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint32_t word = w[k];
+            f[2 * k] = __uint_as_float(word << 16);
+            f[2 * k + 1] = __uint_as_float(word & 0xffff0000u);
+        }
+    } else {
+        widen4<T>(w, f);
+    }
+}
+
 // One 16x16x16 MFMA on raw 16-bit operands (four values per lane).
 template <typename T>
 __device__ __forceinline__ f32x4 mfma16(const u32x2 &a, const u32x2 &b, f32x4 c)
@@ -187,18 +205,42 @@ struct TileState {
     __device__ void update(const f32x4 (&s)[NB], const bool (&live)[NB], bool unmasked, int n0,
                            bool row_ok, int my_pos, float qscale, int gq, float (&p)[NB][4])
     {
+        if (qscale > 0.0f)  // wave-uniform
+            update_impl<NB, true>(s, live, unmasked, n0, row_ok, my_pos, qscale, gq, p);
+        else
+            update_impl<NB, false>(s, live, unmasked, n0, row_ok, my_pos, qscale, gq, p);
+    }
+
+    template <int NB, bool kPos>
+    __device__ void update_impl(const f32x4 (&s)[NB], const bool (&live)[NB], bool unmasked,
+                                int n0, bool row_ok, int my_pos, float qscale, int gq,
+                                float (&p)[NB][4])
+    {
+        // Token 4 gq + i of block bi is kept while 4 gq + i <= lim_b: lim
+        // is this row's last visible position relative to the step's first
+        // token (no limit when unmasked, none visible for a padding row), so
+        // masking is one compare and one select per score, without branches.
+        // With qscale > 0 (every usual scale) the scores stay unscaled until
+        // the exponent, where the scale and the maximum fold into one FMA;
+        // any other scale multiplies first and exponentiates at scale 1.
+        const float post = kPos ? qscale : 1.0f;
+        const int big = NB * kTile;
+        const int lim = unmasked ? big : (row_ok ? min(my_pos - n0 * kTile, big) : -1);
         float bmax = -INFINITY;
 #pragma unroll
-        for (int bi = 0; bi < NB; ++bi)
+        for (int bi = 0; bi < NB; ++bi) {
+            const int lim_b = (live[bi] ? lim : -1) - bi * kTile - 4 * gq;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = (n0 + bi) * kTile + 4 * gq + i;
-                const float v = s[bi][i] * qscale;
-                p[bi][i] = (unmasked || (live[bi] && row_ok && t <= my_pos)) ? v : -INFINITY;
+                const float v = kPos ? s[bi][i] : s[bi][i] * qscale;
+                p[bi][i] = i <= lim_b ? v : -INFINITY;
                 bmax = fmaxf(bmax, p[bi][i]);
             }
+        }
         bmax = allreduce_pair<16, OpMax>(bmax);
         bmax = allreduce_pair<32, OpMax>(bmax);
+        if constexpr (kPos)
+            bmax *= qscale;
         if (__builtin_amdgcn_ballot_w64(bmax > m_run + kSlack) != 0) {
             const float m_new = fmaxf(m_run, bmax);
             const float m_use = m_new == -INFINITY ? 0.0f : m_new;
@@ -215,7 +257,7 @@ struct TileState {
         for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[bi][i] = __builtin_amdgcn_exp2f(p[bi][i] - m_use);
+                p[bi][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[bi][i], post, -m_use));
                 psum += p[bi][i];
             }
         l_lane += psum;
@@ -229,7 +271,7 @@ struct TileState {
         static_assert(EB == 2, "transposing LDS reads are 16-bit");
         const u32x2 p_hi = round4<T>(p);
         float hi[4], lo[4];
-        widen4<T>(p_hi, hi);
+        widen_packed<T>(p_hi, hi);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             lo[i] = p[i] - hi[i];
@@ -631,13 +673,22 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
     // this thread covers K (first half of the chunks) or V, row c / CH,
     // 16-byte column c % CH; blocks at or past n_end read as zero rows.
     const size_t tile_elems = (size_t)kTile * D;
+    // Block-table window: lane i holds the entry of block win0 + i (0 past
+    // the split), so a step's block ids need no dependent memory access.
+    int win0 = n_begin, tbl_win = 0;
+    auto load_window = [&](int n) {
+        win0 = n;
+        tbl_win = n + lane < n_end ? a.block_tables[(size_t)b * a.max_blocks + n + lane] : 0;
+    };
+    load_window(n_begin);
     auto gload = [&](int n0, u32x4 (&regs)[NB][PER]) {
+        if (n0 + NB - 1 - win0 >= 64)
+            load_window(n0);
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi) {
             const int n = n0 + bi;
             const bool live = n < n_end;
-            const int blk = __builtin_amdgcn_readfirstlane(
-                a.block_tables[(size_t)b * a.max_blocks + (live ? n : n0)]);
+            const int blk = __builtin_amdgcn_readlane(tbl_win, (live ? n : n0) - win0);
             const int valid = live ? min(kTile, scan_end - n * kTile) : 0;
             const size_t base = ((size_t)blk * hkv + g) * tile_elems;
             const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(

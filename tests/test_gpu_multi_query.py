@@ -153,6 +153,21 @@ def test_repeat_is_bit_identical(pa):
     assert a.tobytes() == b.tobytes()
 
 
+@pytest.mark.parametrize("dtype", [np.float32, di.BF16])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.7])
+@pytest.mark.parametrize("longest", [2, 40])
+def test_any_finite_scale(pa, dtype, scale, longest):
+    # positive scales fold into the exponent, others are applied first; a
+    # zero scale averages the visible rows.  A longest query run of 2 tokens
+    # (8 rows) runs the per-tile kernel, one of 40 (160 rows) the wide one.
+    rng = np.random.default_rng(630)
+    qlens, ctx = [3 if longest > 3 else 1, longest, 1], [300, 900, 17]
+    q, kc, vc, tables, ctx, qs = ragged_case(rng, dtype, qlens, ctx, 8, 2, 64, 16)
+    ref = oracle.paged_attn_multi_query(q, kc, vc, tables, ctx, qs, scale)
+    got = gpu_mq(pa, q, kc, vc, tables, ctx, qs, scale)
+    assert_close(got, ref, dtype, f"scale {scale}")
+
+
 @pytest.mark.parametrize("split", [0, 64, 128, 512, 4096])
 def test_kv_split_sizes_agree_with_oracle(pa, split):
     # long contexts with short and long query runs: many tiles span several
