@@ -188,6 +188,32 @@ struct TileState {
         return s;
     }
 
+    // Scores of NB blocks at once, the blocks' MFMA chains interleaved so
+    // that no MFMA waits on the one before it.
+    template <int NB>
+    __device__ static void scores_blocks(const uint32_t (&kw)[NB][NW], const uint32_t (&qw)[NW],
+                                         f32x4 (&s)[NB])
+    {
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+            s[bi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (EB == 4) {
+#pragma unroll
+            for (int k = 0; k < QD; ++k)
+#pragma unroll
+                for (int bi = 0; bi < NB; ++bi)
+                    s[bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[bi][k]),
+                                                                 __uint_as_float(qw[k]), s[bi], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int k = 0; k < QD / 4; ++k)
+#pragma unroll
+                for (int bi = 0; bi < NB; ++bi)
+                    s[bi] = mfma16<T>(u32x2{kw[bi][2 * k], kw[bi][2 * k + 1]},
+                                      u32x2{qw[2 * k], qw[2 * k + 1]}, s[bi]);
+        }
+    }
+
     // One softmax update over NB blocks n0 .. n0 + NB - 1 (those with
     // live[bi]): scores in log2 units, tokens past my_pos (or any token of a
     // padding row) masked, unless `unmasked` says every token of the blocks
@@ -277,12 +303,18 @@ struct TileState {
             lo[i] = p[i] - hi[i];
         const u32x2 p_lo = round4<T>(lo);
         const T *src = &v[(4 * gq + (lr >> 2)) * ks + 4 * (lr & 3)];
+        u32x2 va[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const u32x2 va = lds_read_transposed(src + 16 * t);
-            o_acc[t] = mfma16<T>(va, p_hi, o_acc[t]);
-            o_acc[t] = mfma16<T>(va, p_lo, o_acc[t]);
-        }
+        for (int t = 0; t < MT; ++t)
+            va[t] = lds_read_transposed(src + 16 * t);
+        // all tiles' first halves, then the residuals: consecutive MFMAs
+        // never feed each other
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            o_acc[t] = mfma16<T>(va[t], p_hi, o_acc[t]);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            o_acc[t] = mfma16<T>(va[t], p_lo, o_acc[t]);
     }
 
     // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS.
@@ -754,27 +786,27 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
         if (more)
             gload(n0 + NB, regs);  // in flight while these blocks are used
         if (has_rows && n0 * kTile <= wave_last_pos) {
-            // scores of the step's blocks, one softmax update, then P.V
+            // Scores of all the step's blocks, one softmax update, then
+            // P.V.  Blocks that no row of this wave reaches (past its last
+            // position, or past the split: zero rows in LDS) are computed
+            // too, without branches; their weights are exactly zero.
             f32x4 sc[NB];
             bool live[NB];
+            uint32_t kw[NB][NW];
 #pragma unroll
             for (int bi = 0; bi < NB; ++bi) {
                 const int n = n0 + bi;
                 live[bi] = n < n_end && n * kTile <= wave_last_pos;  // wave-uniform
-                sc[bi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                if (live[bi]) {
-                    uint32_t kw[NW];
-                    const T *krow = &kl[buf][(bi * kTile + lr) * KS + gq * QD];
+                const T *krow = &kl[buf][(bi * kTile + lr) * KS + gq * QD];
 #pragma unroll
-                    for (int i = 0; i < NL; ++i) {
-                        const u32x4 v = reinterpret_cast<const u32x4 *>(krow)[i];
+                for (int i = 0; i < NL; ++i) {
+                    const u32x4 v = reinterpret_cast<const u32x4 *>(krow)[i];
 #pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            kw[4 * i + k] = v[k];
-                    }
-                    sc[bi] = TS::scores(kw, qw);
+                    for (int k = 0; k < 4; ++k)
+                        kw[bi][4 * i + k] = v[k];
                 }
             }
+            TS::template scores_blocks<NB>(kw, qw, sc);
             float p[NB][4];
             bool all_live = true;
 #pragma unroll
@@ -783,13 +815,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
             const bool unmasked = all_live && (n0 + NB) * kTile - 1 <= wave_first_pos;
             st.template update<NB>(sc, live, unmasked, n0, row_ok, my_pos, a.qscale, gq, p);
 #pragma unroll
-            for (int bi = 0; bi < NB; ++bi)
-                if (live[bi]) {
-                    if constexpr (kRowV)
-                        st.pv_rows(&vtl[buf][bi * VBLK], KS, lr, gq, p[bi]);
-                    else
-                        st.pv(&vtl[buf][bi * VBLK], lr, gq, p[bi]);
-                }
+            for (int bi = 0; bi < NB; ++bi) {
+                if constexpr (kRowV)
+                    st.pv_rows(&vtl[buf][bi * VBLK], KS, lr, gq, p[bi]);
+                else
+                    st.pv(&vtl[buf][bi * VBLK], lr, gq, p[bi]);
+            }
         }
         if (more)
             lstore(buf ^ 1, regs);
