@@ -108,6 +108,24 @@ __device__ __forceinline__ void widen4(const u32x2 &w, float (&f)[4])
     }
 }
 
+// One 16x16x32 MFMA on raw 16-bit operands (eight values per lane; gfx950).
+// Lane l holds A[m = l % 16][k = 8 (l / 16) + i] and B[k][n = l % 16] for
+// i < 8, and receives D[4 (l / 16) + i][l % 16] as the 16x16x16 form does
+// (checked with an in-bounds probe).
+template <typename T>
+__device__ __forceinline__ f32x4 mfma32(const u32x4 &a, const u32x4 &b, f32x4 c)
+{
+    if constexpr (__is_same(T, _Float16)) {
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a),
+                                                      __builtin_bit_cast(h8, b), c, 0, 0, 0);
+    } else {
+        typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a),
+                                                       __builtin_bit_cast(b8, b), c, 0, 0, 0);
+    }
+}
+
 // widen4 written on the packed bits: bfloat16 widens by a shift or a mask
 // of the word it was packed in (so the compiler does not re-round the fp32
 // source); binary16 converts each half.
@@ -205,12 +223,16 @@ struct TileState {
                     s[bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[bi][k]),
                                                                  __uint_as_float(qw[k]), s[bi], 0, 0, 0);
         } else {
+            // K = 32 per MFMA: a lane's head-dimension elements 8 c .. 8 c + 7
+            // of its quarter feed MFMA c, the same ones from K and from Q.
 #pragma unroll
-            for (int k = 0; k < QD / 4; ++k)
+            for (int c = 0; c < QD / 8; ++c)
 #pragma unroll
                 for (int bi = 0; bi < NB; ++bi)
-                    s[bi] = mfma16<T>(u32x2{kw[bi][2 * k], kw[bi][2 * k + 1]},
-                                      u32x2{qw[2 * k], qw[2 * k + 1]}, s[bi]);
+                    s[bi] = mfma32<T>(u32x4{kw[bi][4 * c], kw[bi][4 * c + 1], kw[bi][4 * c + 2],
+                                            kw[bi][4 * c + 3]},
+                                      u32x4{qw[4 * c], qw[4 * c + 1], qw[4 * c + 2], qw[4 * c + 3]},
+                                      s[bi]);
         }
     }
 
@@ -307,14 +329,13 @@ struct TileState {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
             va[t] = lds_read_transposed(src + 16 * t);
-        // all tiles' first halves, then the residuals: consecutive MFMAs
-        // never feed each other
+        // One K = 32 MFMA per tile takes both parts of the weights: k = 4 g + i
+        // pairs token 4 g + i with its rounded weight, k = 4 g + 4 + i with
+        // its residual, so the A operand is the same four V values twice.
+        const u32x4 pb{p_hi[0], p_hi[1], p_lo[0], p_lo[1]};
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-            o_acc[t] = mfma16<T>(va[t], p_hi, o_acc[t]);
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-            o_acc[t] = mfma16<T>(va[t], p_lo, o_acc[t]);
+            o_acc[t] = mfma32<T>(u32x4{va[t][0], va[t][1], va[t][0], va[t][1]}, pb, o_acc[t]);
     }
 
     // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS.
