@@ -273,18 +273,27 @@ struct TileState {
         // any other scale multiplies first and exponentiates at scale 1.
         const float post = kPos ? qscale : 1.0f;
         const int big = NB * kTile;
-        const int lim = unmasked ? big : (row_ok ? min(my_pos - n0 * kTile, big) : -1);
+        const int lim = row_ok ? min(my_pos - n0 * kTile, big) : -1;
         float bmax = -INFINITY;
 #pragma unroll
-        for (int bi = 0; bi < NB; ++bi) {
-            const int lim_b = (live[bi] ? lim : -1) - bi * kTile - 4 * gq;
+        for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = kPos ? s[bi][i] : s[bi][i] * qscale;
-                p[bi][i] = i <= lim_b ? v : -INFINITY;
-                bmax = fmaxf(bmax, p[bi][i]);
+            for (int i = 0; i < 4; ++i)
+                p[bi][i] = kPos ? s[bi][i] : s[bi][i] * qscale;
+        if (!unmasked) {  // wave-uniform; most steps of a long run need no mask
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi) {
+                const int lim_b = (live[bi] ? lim : -1) - bi * kTile - 4 * gq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p[bi][i] = i <= lim_b ? p[bi][i] : -INFINITY;
             }
         }
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bmax = fmaxf(bmax, p[bi][i]);
         bmax = allreduce_pair<16, OpMax>(bmax);
         bmax = allreduce_pair<32, OpMax>(bmax);
         if constexpr (kPos)
@@ -336,6 +345,45 @@ struct TileState {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
             o_acc[t] = mfma32<T>(u32x4{va[t][0], va[t][1], va[t][0], va[t][1]}, pb, o_acc[t]);
+    }
+
+    // The same for two blocks at once (v1 = the second block's tile): K = 32
+    // pairs k = 4 g + i with token 4 g + i of the first block and
+    // k = 4 g + 4 + i with that of the second, so each tile's A operand is
+    // two transposing reads side by side; rounded weights and residuals
+    // take one MFMA each.
+    __device__ void pv_rows2(const T *v0, const T *v1, int ks, int lr, int gq, const float (&p0)[4],
+                             const float (&p1)[4])
+    {
+        static_assert(EB == 2, "transposing LDS reads are 16-bit");
+        u32x2 hi[2], lo[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float(&p)[4] = j == 0 ? p0 : p1;
+            hi[j] = round4<T>(p);
+            float h[4], l[4];
+            widen_packed<T>(hi[j], h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                l[i] = p[i] - h[i];
+            lo[j] = round4<T>(l);
+        }
+        const int off = (4 * gq + (lr >> 2)) * ks + 4 * (lr & 3);
+        u32x4 va[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const u32x2 a0 = lds_read_transposed(v0 + off + 16 * t);
+            const u32x2 a1 = lds_read_transposed(v1 + off + 16 * t);
+            va[t] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        }
+        const u32x4 bh{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
+        const u32x4 bl{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            o_acc[t] = mfma32<T>(va[t], bh, o_acc[t]);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            o_acc[t] = mfma32<T>(va[t], bl, o_acc[t]);
     }
 
     // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS.
@@ -835,11 +883,15 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
                 all_live = all_live && live[bi];
             const bool unmasked = all_live && (n0 + NB) * kTile - 1 <= wave_first_pos;
             st.template update<NB>(sc, live, unmasked, n0, row_ok, my_pos, a.qscale, gq, p);
+            if constexpr (kRowV) {
+                static_assert(NB % 2 == 0, "16-bit steps hold whole block pairs");
 #pragma unroll
-            for (int bi = 0; bi < NB; ++bi) {
-                if constexpr (kRowV)
-                    st.pv_rows(&vtl[buf][bi * VBLK], KS, lr, gq, p[bi]);
-                else
+                for (int bi = 0; bi < NB; bi += 2)
+                    st.pv_rows2(&vtl[buf][bi * VBLK], &vtl[buf][(bi + 1) * VBLK], KS, lr, gq,
+                                p[bi], p[bi + 1]);
+            } else {
+#pragma unroll
+                for (int bi = 0; bi < NB; ++bi)
                     st.pv(&vtl[buf][bi * VBLK], lr, gq, p[bi]);
             }
         }
