@@ -782,60 +782,58 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
         tbl_win = n + lane < n_end ? a.block_tables[(size_t)b * a.max_blocks + n + lane] : 0;
     };
     load_window(n_begin);
-    auto gload = [&](int n0, u32x4 (&regs)[NB][PER]) {
+    // Each wave loads one contiguous quarter of the step's chunks, which lies
+    // inside one block (K part or V part), so a wave sets up one block's
+    // descriptors per step: lane l takes chunk c0 + 64 i + l.
+    constexpr int CPW = NB * NCH / kMqWaves;  // chunks per wave per step
+    constexpr int PW = CPW / 64;              // 16-byte loads per lane per step
+    static_assert(CPW % 64 == 0 && NCH % CPW == 0, "a wave's chunks lie in one block");
+    const int c0 = wave * CPW;
+    const int wbi = c0 / NCH;  // the wave's block within the step
+    auto gload = [&](int n0, u32x4 (&regs)[PW]) {
         if (n0 + NB - 1 - win0 >= 64)
             load_window(n0);
+        const int n = n0 + wbi;
+        const bool live = n < n_end;
+        const int blk = __builtin_amdgcn_readlane(tbl_win, (live ? n : n0) - win0);
+        const int valid = live ? min(kTile, scan_end - n * kTile) : 0;
+        const size_t base = ((size_t)blk * hkv + g) * tile_elems;
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const T *)a.k_cache + base), (short)0, valid * D * EB, kRawWord3);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const T *)a.v_cache + base), (short)0, valid * D * EB, kRawWord3);
 #pragma unroll
-        for (int bi = 0; bi < NB; ++bi) {
-            const int n = n0 + bi;
-            const bool live = n < n_end;
-            const int blk = __builtin_amdgcn_readlane(tbl_win, (live ? n : n0) - win0);
-            const int valid = live ? min(kTile, scan_end - n * kTile) : 0;
-            const size_t base = ((size_t)blk * hkv + g) * tile_elems;
-            const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)((const T *)a.k_cache + base), (short)0, valid * D * EB, kRawWord3);
-            const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)((const T *)a.v_cache + base), (short)0, valid * D * EB, kRawWord3);
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int c = threadIdx.x + i * kMqWaves * 64;
-                const int rc = c % (kTile * CH);
-                // K and V chunks split at a multiple of 64, so a wave loads
-                // only one of them: keep the descriptor choice scalar.
-                const bool is_k = __builtin_amdgcn_readfirstlane(c < kTile * CH ? 1 : 0) != 0;
-                regs[bi][i] = __builtin_amdgcn_raw_buffer_load_b128(is_k ? krs : vrs, rc * 16, 0, 0);
-            }
+        for (int i = 0; i < PW; ++i) {
+            const int cc = c0 % NCH + i * 64;  // wave-uniform; K and V split at a multiple of 64
+            const bool is_k = cc < kTile * CH;
+            const int rc = cc % (kTile * CH) + lane;
+            regs[i] = __builtin_amdgcn_raw_buffer_load_b128(is_k ? krs : vrs, rc * 16, 0, 0);
         }
     };
-    auto lstore = [&](int buf, const u32x4 (&regs)[NB][PER]) {
+    auto lstore = [&](int buf, const u32x4 (&regs)[PW]) {
+        T *kb = &kl[buf][wbi * kTile * KS];
+        T *vb = &vtl[buf][wbi * VBLK];
 #pragma unroll
-        for (int bi = 0; bi < NB; ++bi) {
-            T *kb = &kl[buf][bi * kTile * KS];
-            T *vb = &vtl[buf][bi * VBLK];
+        for (int i = 0; i < PW; ++i) {
+            const int cc = c0 % NCH + i * 64;
+            const int rc = cc % (kTile * CH) + lane;
+            const int row = rc / CH, col = rc % CH;
+            if (cc < kTile * CH) {
+                *reinterpret_cast<u32x4 *>(&kb[row * KS + col * EC]) = regs[i];
+            } else if constexpr (kRowV) {
+                *reinterpret_cast<u32x4 *>(&vb[row * KS + col * EC]) = regs[i];
+            } else {
+                const u32x4 w = regs[i];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int c = threadIdx.x + i * kMqWaves * 64;
-                if (c >= NCH)
-                    break;
-                const int rc = c % (kTile * CH);
-                const int row = rc / CH, col = rc % CH;
-                if (__builtin_amdgcn_readfirstlane(c < kTile * CH ? 1 : 0) != 0) {
-                    *reinterpret_cast<u32x4 *>(&kb[row * KS + col * EC]) = regs[bi][i];
-                } else if constexpr (kRowV) {
-                    *reinterpret_cast<u32x4 *>(&vb[row * KS + col * EC]) = regs[bi][i];
-                } else {
-                    const u32x4 w = regs[bi][i];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t word = w[k];
-                        if constexpr (EB == 4) {
-                            vb[(col * EC + k) * VS + row] = __builtin_bit_cast(T, word);
-                        } else {
-                            typedef T t2 __attribute__((ext_vector_type(2)));
-                            const t2 pair = __builtin_bit_cast(t2, word);
-                            vb[(col * EC + 2 * k) * VS + row] = pair[0];
-                            vb[(col * EC + 2 * k + 1) * VS + row] = pair[1];
-                        }
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t word = w[k];
+                    if constexpr (EB == 4) {
+                        vb[(col * EC + k) * VS + row] = __builtin_bit_cast(T, word);
+                    } else {
+                        typedef T t2 __attribute__((ext_vector_type(2)));
+                        const t2 pair = __builtin_bit_cast(t2, word);
+                        vb[(col * EC + 2 * k) * VS + row] = pair[0];
+                        vb[(col * EC + 2 * k + 1) * VS + row] = pair[1];
                     }
                 }
             }
@@ -843,7 +841,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
     };
 
     TS st;
-    u32x4 regs[NB][PER];
+    u32x4 regs[PW];
     if (n_begin < n_end) {
         gload(n_begin, regs);
         lstore(0, regs);
