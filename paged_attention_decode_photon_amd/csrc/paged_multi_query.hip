@@ -135,7 +135,10 @@ __device__ __forceinline__ void widen_packed(const u32x2 &w, float (&f)[4])
     if constexpr (__is_same(T, __bf16)) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const uint32_t word = w[k];
+            uint32_t word = w[k];
+            // hide the word's origin: otherwise the compiler re-rounds the
+            // low half's source value instead of shifting the packed word
+            asm("" : "+v"(word));
             f[2 * k] = __uint_as_float(word << 16);
             f[2 * k + 1] = __uint_as_float(word & 0xffff0000u);
         }
@@ -309,14 +312,18 @@ struct TileState {
                 o_acc[t] *= alpha;
         }
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        float psum = 0.0f;
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i)
                 p[bi][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[bi][i], post, -m_use));
-                psum += p[bi][i];
-            }
+        float psum = p[0][0];
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (bi != 0 || i != 0)
+                    psum += p[bi][i];
         l_lane += psum;
     }
 
@@ -716,7 +723,8 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
     // 16-bit V stays row-major (like K) and is read back through the
     // transposing LDS read; fp32 V is stored transposed.
     constexpr bool kRowV = EB == 2;
-    constexpr int VBLK = kRowV ? kTile * KS : D * VS;  // LDS elements of one V block
+    constexpr int VKS = KS;  // row stride of a row-major V tile
+    constexpr int VBLK = kRowV ? kTile * VKS : D * VS;  // LDS elements of one V block
     __shared__ __attribute__((aligned(16))) T kl[2][NB * kTile * KS];
     __shared__ __attribute__((aligned(16))) T vtl[2][NB * VBLK];
 
@@ -821,7 +829,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
             if (cc < kTile * CH) {
                 *reinterpret_cast<u32x4 *>(&kb[row * KS + col * EC]) = regs[i];
             } else if constexpr (kRowV) {
-                *reinterpret_cast<u32x4 *>(&vb[row * KS + col * EC]) = regs[i];
+                *reinterpret_cast<u32x4 *>(&vb[row * VKS + col * EC]) = regs[i];
             } else {
                 const u32x4 w = regs[i];
 #pragma unroll
@@ -885,7 +893,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
                 static_assert(NB % 2 == 0, "16-bit steps hold whole block pairs");
 #pragma unroll
                 for (int bi = 0; bi < NB; bi += 2)
-                    st.pv_rows2(&vtl[buf][bi * VBLK], &vtl[buf][(bi + 1) * VBLK], KS, lr, gq,
+                    st.pv_rows2(&vtl[buf][bi * VBLK], &vtl[buf][(bi + 1) * VBLK], VKS, lr, gq,
                                 p[bi], p[bi + 1]);
             } else {
 #pragma unroll
