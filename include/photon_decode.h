@@ -103,7 +103,9 @@ typedef struct photon_decode_desc {
                                    max_context_len, a positive multiple of
                                    photon_paged_attn_partition_quantum(); the
                                    actual batch is always split evenly over
-                                   the wavefronts this implies                   */
+                                   the wavefronts this implies, but over no
+                                   more than one per five quanta of it (a
+                                   slice is never much shorter than five)      */
     photon_kv_desc kv;
     int32_t flags;              /* PHOTON_DECODE_* bits, 0 = none; other bits
                                    are PHOTON_ERR_INVALID_ARG                    */
