@@ -290,6 +290,11 @@ struct WaveDecoder {
         for (int i = 0; i < NU; ++i)
             vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rv[i / NIB], v_off[i % NIB], 0,
                                                           PHOTON_KV_LOAD_AUX);
+        // 16-bit chunks: keep every K and V load of the chunk ahead of the
+        // math (the scheduler otherwise sinks part of V behind the scores,
+        // which costs a second round trip per chunk).
+        if constexpr (S::EB == 2)
+            __builtin_amdgcn_sched_barrier(0);
     }
 
     // Scores, online softmax update and P.V for chunk ch.
@@ -380,18 +385,42 @@ struct WaveDecoder {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // Chunks [ch0, ch1) of the current segment, one at a time.  (Loading the
-    // next chunk before consuming the current one measured slower: the extra
-    // registers cost occupancy and the loads in flight per CU do not grow.)
+    __device__ void issue_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU])
+    {
+        cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
+        if (new_pos >= ch * CT && new_pos < (ch + 1) * CT)
+            store_new_token();
+        load_chunk(ch, kd, vd);
+    }
+
+    // Chunks [ch0, ch1) of the current segment.  With 16-bit storage a chunk
+    // is only 8 KiB per wave, too little in flight to cover the memory
+    // latency, so the next chunk is loaded before the current one is used
+    // (two register sets, alternating).  fp32 chunks (16 KiB) already keep
+    // HBM busy and go one at a time (two in flight measured slower there).
     __device__ void run_chunks(int ch0, int ch1)
     {
-        for (int ch = ch0; ch < ch1; ++ch) {
-            cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
-            if (new_pos >= ch * CT && new_pos < (ch + 1) * CT)
-                store_new_token();
-            u32x4 kd[NU], vd[NU];
-            load_chunk(ch, kd, vd);
-            consume_chunk(ch, kd, vd);
+        if constexpr (S::EB == 2) {
+            u32x4 ka[NU], va[NU], kb[NU], vb[NU];
+            issue_chunk(ch0, ka, va);
+            for (int ch = ch0;;) {
+                if (ch + 1 < ch1)
+                    issue_chunk(ch + 1, kb, vb);
+                consume_chunk(ch, ka, va);
+                if (++ch >= ch1)
+                    break;
+                if (ch + 1 < ch1)
+                    issue_chunk(ch + 1, ka, va);
+                consume_chunk(ch, kb, vb);
+                if (++ch >= ch1)
+                    break;
+            }
+        } else {
+            for (int ch = ch0; ch < ch1; ++ch) {
+                u32x4 kd[NU], vd[NU];
+                issue_chunk(ch, kd, vd);
+                consume_chunk(ch, kd, vd);
+            }
         }
     }
 
