@@ -515,10 +515,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     const int tile_first_pos = first_pos + (tile * kTile) / G;  // the tile's earliest row
     const size_t tile_elems = (size_t)kTile * D;
 
-    // Issue the K and V loads of block n (zero rows when !live).
-    auto load_block = [&](int n, bool live, uint32_t (&kw)[NW], uint32_t (&vw)[NW]) {
+    // Issue the K and V loads of block n (rows past scan_end read as zero).
+    auto load_block = [&](int n, uint32_t (&kw)[NW], uint32_t (&vw)[NW]) {
         const int blk = __builtin_amdgcn_readfirstlane(a.block_tables[(size_t)b * a.max_blocks + n]);
-        const int valid = live ? min(kTile, scan_end - n * kTile) : 0;
+        const int valid = min(kTile, scan_end - n * kTile);
         const size_t base = ((size_t)blk * hkv + g) * tile_elems;
         const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const T *)a.k_cache + base), (short)0, valid * D * EB, kRawWord3);
@@ -563,17 +563,29 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         wave_sync();  // reads of the V tile are done before the next block overwrites it
     };
 
-    // Two of this wave's blocks per step, both loaded before either is used,
-    // so each wave keeps two blocks of K and V in flight.
-    for (int n = n_begin + wave; n < n_end; n += 2 * kMqWaves) {
-        const int n2 = n + kMqWaves;
-        const bool two = n2 < n_end;
+    // This wave's blocks n_begin + wave + 4 j, two in flight at all times:
+    // each block's registers are refilled with the block after next as soon
+    // as the block has been used.
+    {
+        constexpr int S = kMqWaves;
         uint32_t ka[NW], va[NW], kb[NW], vb[NW];
-        load_block(n, true, ka, va);
-        load_block(two ? n2 : n, two, kb, vb);
-        compute_block(n, ka, va);
-        if (two)
-            compute_block(n2, kb, vb);
+        int n = n_begin + wave;
+        if (n < n_end)
+            load_block(n, ka, va);
+        if (n + S < n_end)
+            load_block(n + S, kb, vb);
+        while (n < n_end) {
+            compute_block(n, ka, va);
+            if (n + 2 * S < n_end)
+                load_block(n + 2 * S, ka, va);
+            n += S;
+            if (n >= n_end)
+                break;
+            compute_block(n, kb, vb);
+            if (n + 2 * S < n_end)
+                load_block(n + 2 * S, kb, vb);
+            n += S;
+        }
     }
 
     // Merge the four waves' partial states of each row.
