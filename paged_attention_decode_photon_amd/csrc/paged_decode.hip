@@ -469,14 +469,14 @@ struct WaveDecoder {
                 o_acc[h][e] = allreduce_bits<S::LOG2L, 6, OpSum>(o_acc[h][e]);
     }
 
-    __device__ O *out_rows() const
+    __device__ O *out_rows(int b_, int g_) const
     {
-        return (O *)a.out + ((size_t)b * a.num_kv_heads * G + (size_t)g * G) * D;
+        return (O *)a.out + ((size_t)b_ * a.num_kv_heads * G + (size_t)g_ * G) * D;
     }
 
     __device__ void write_output() const
     {
-        O *dst = out_rows();
+        O *dst = out_rows(b, g);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float inv = 1.0f / read_lane(l_run, h);
@@ -516,16 +516,16 @@ struct WaveDecoder {
         }
     }
 
-    // Merge the records of every piece of segment (b, g), units [su0, su1),
+    // Merge the records of every piece of segment (sb, sg), units [su0, su1),
     // in slice order, and write the normalised output.  Each lane folds four
     // consecutive outputs of one head; kBatch records are loaded at a time.
-    __device__ void merge_segment(int su0, int su1, int total, int nw) const
+    __device__ void merge_segment(int sb, int sg, int su0, int su1, int total, int nw) const
     {
         constexpr int kBatch = 8;
         const int s_first = slice_of(su0, total, nw);
         const int s_last = slice_of(su1 - 1, total, nw);
         const int first_role = slice_start(s_first, total, nw) == su0 ? 0 : 1;
-        O *dst = out_rows();
+        O *dst = out_rows(sb, sg);
         compiler_memory_barrier();
         for (int v = lane; v < G * D / 4; v += 64) {
             const int i = 4 * v;  // first of this lane's four outputs
@@ -678,6 +678,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     }
     int b = lo;
     int u = u_begin;
+    // A first piece that ends inside the slice leaves its arrival pending:
+    // it is counted once the next piece's first loads are on their way, so
+    // the record stores complete during that round trip instead of stalling
+    // the wave, and the count's result is only read at the end (merging
+    // then, should this wave have completed the segment).
+    bool pend = false, pend_count_now = false;
+    int pend_b = 0, pend_g = 0, pend_seg = 0, pend_nch = 0, pend_units = 0, pend_old = 0;
     while (u < u_end) {
         const int seq_end = __builtin_amdgcn_readfirstlane(unit_end[b]);
         const int ctx = __builtin_amdgcn_readfirstlane(ctx_lds[b]);
@@ -694,6 +701,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         const bool appends = a.k_new != nullptr && ch1 == nch;
         if (appends)
             w.prepare_new_token();
+        if (pend_count_now) {
+            // the record stores before, this piece's window and query loads
+            // after: one wait covers both, then the arrival counts
+            wait_vector_memory();
+            int old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(&a.ws_count[(size_t)pend_b * hkv + pend_g], pend_units,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pend_old = old;
+            pend_count_now = false;
+        }
         w.run_chunks(ch0, ch1);
         w.reduce_piece();
         if (ch0 == 0 && ch1 == nch) {
@@ -701,17 +719,26 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         } else {
             const int role = (u == u_begin) ? 0 : 1;
             w.store_record(a.ws_rec + ((size_t)s * 2 + role) * S::REC);
-            wait_vector_memory();
-            int done = 0;
-            if (lane == 0)
-                done = __hip_atomic_fetch_add(&a.ws_count[(size_t)b * hkv + g], ch1 - ch0,
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            done = __builtin_amdgcn_readfirstlane(done) + (ch1 - ch0);
-            if (done == nch) {
-                w.merge_segment(seg_begin, seg_end, total, nw);
+            if (piece_end < u_end) {  // only a slice's first piece ends early
+                pend = pend_count_now = true;
+                pend_b = b;
+                pend_g = g;
+                pend_seg = seg_begin;
+                pend_nch = nch;
+                pend_units = ch1 - ch0;
+            } else {
+                wait_vector_memory();
+                int done = 0;
                 if (lane == 0)
-                    __hip_atomic_store(&a.ws_count[(size_t)b * hkv + g], 0, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                    done = __hip_atomic_fetch_add(&a.ws_count[(size_t)b * hkv + g], ch1 - ch0,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                done = __builtin_amdgcn_readfirstlane(done) + (ch1 - ch0);
+                if (done == nch) {
+                    w.merge_segment(b, g, seg_begin, seg_end, total, nw);
+                    if (lane == 0)
+                        __hip_atomic_store(&a.ws_count[(size_t)b * hkv + g], 0, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
         u = piece_end;
@@ -720,6 +747,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
             while (b < B && __builtin_amdgcn_readfirstlane(unit_end[b]) == u)
                 ++b;
         }
+    }
+    if (pend && __builtin_amdgcn_readfirstlane(pend_old) + pend_units == pend_nch) {
+        w.merge_segment(pend_b, pend_g, pend_seg, pend_seg + pend_nch, total, nw);
+        if (lane == 0)
+            __hip_atomic_store(&a.ws_count[(size_t)pend_b * hkv + pend_g], 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
