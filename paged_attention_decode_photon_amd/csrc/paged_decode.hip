@@ -290,11 +290,10 @@ struct WaveDecoder {
         for (int i = 0; i < NU; ++i)
             vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rv[i / NIB], v_off[i % NIB], 0,
                                                           PHOTON_KV_LOAD_AUX);
-        // 16-bit chunks: keep every K and V load of the chunk ahead of the
-        // math (the scheduler otherwise sinks part of V behind the scores,
-        // which costs a second round trip per chunk).
-        if constexpr (S::EB == 2)
-            __builtin_amdgcn_sched_barrier(0);
+        // Keep every K and V load of the chunk ahead of the math (the
+        // scheduler otherwise sinks part of V behind the scores, which costs
+        // a second round trip per chunk).
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // Scores, online softmax update and P.V for chunk ch.
@@ -393,14 +392,14 @@ struct WaveDecoder {
         load_chunk(ch, kd, vd);
     }
 
-    // Chunks [ch0, ch1) of the current segment.  With 16-bit storage a chunk
-    // is only 8 KiB per wave, too little in flight to cover the memory
-    // latency, so the next chunk is loaded before the current one is used
-    // (two register sets, alternating).  fp32 chunks (16 KiB) already keep
-    // HBM busy and go one at a time (two in flight measured slower there).
+    // Chunks [ch0, ch1) of the current segment, two in flight: the next
+    // chunk is loaded before the current one is used (two register sets,
+    // alternating).  With eight query heads per KV head the second set would
+    // take the kernel past 256 VGPRs, i.e. below the two waves per SIMD the
+    // automatic plan launches for 16-bit storage; those go one at a time.
     __device__ void run_chunks(int ch0, int ch1)
     {
-        if constexpr (S::EB == 2) {
+        if constexpr (G < 8) {
             u32x4 ka[NU], va[NU], kb[NU], vb[NU];
             issue_chunk(ch0, ka, va);
             for (int ch = ch0;;) {
