@@ -189,6 +189,8 @@ struct WaveDecoder {
     int b, g, ctx;
     int new_pos;         // fused step: position of the appended token, else -1
     u32x4 knew, vnew;    // fused step: this lane's column of the new K and V rows
+    bool append_pending = false;  // the new rows are loaded but not yet stored
+    bool append_settled = true;   // a chunk loaded after the stores has been used
     int nblk;      // blocks holding the sequence's context
     int win0;      // first block index of the table window
     int tbl_win;   // lane i: block_tables[b][win0 + i] (0 past the context)
@@ -382,13 +384,21 @@ struct WaveDecoder {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        append_settled = true;  // this chunk's loads are done, and so are older stores
     }
 
     __device__ void issue_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU])
     {
         cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
-        if (new_pos >= ch * CT && new_pos < (ch + 1) * CT)
+        if (append_pending) {  // the piece's first chunk: store the new row now
             store_new_token();
+            append_pending = false;
+            append_settled = false;
+        }
+        // The chunk that holds the new row must see it: the stores are done
+        // once any chunk issued after them has been used, else wait here.
+        if (new_pos >= ch * CT && new_pos < (ch + 1) * CT && !append_settled)
+            wait_vector_memory();
         load_chunk(ch, kd, vd);
     }
 
@@ -426,22 +436,26 @@ struct WaveDecoder {
     // Fused decode step.  The segment's new K and V rows belong at position
     // ctx - 1, inside the segment's last chunk, which only this wave reads.
     // Each lane takes its 16-byte column of both rows from k_new / v_new when
-    // the piece starts; right before the chunk that holds the position the
-    // rows are stored to the pool and the wave waits for its stores, so that
-    // chunk's loads see them.  By then the column loads have long arrived
-    // unless that chunk is the piece's first.
+    // the piece starts and stores them to the pool just before the piece's
+    // first chunk is loaded.  Stores and loads complete in order, so once a
+    // chunk loaded after the stores has been used the stores are done; the
+    // chunk holding the position waits for them only if none has (a piece of
+    // one or two chunks).
     __device__ void prepare_new_token()
     {
         const size_t src = ((size_t)b * a.num_kv_heads + g) * D + c * E;
         knew = *reinterpret_cast<const u32x4 *>((const T *)a.k_new + src);
         vnew = *reinterpret_cast<const u32x4 *>((const T *)a.v_new + src);
         new_pos = ctx - 1;
+        append_pending = true;
     }
 
     __device__ void store_new_token() const
     {
-        const int blk = __builtin_amdgcn_readfirstlane(
-            a.block_tables[(size_t)b * a.max_blocks + new_pos / kBlockTokens]);
+        const int n = new_pos / kBlockTokens;
+        const int blk = n - win0 < 64 ? block_at(n)
+                                      : __builtin_amdgcn_readfirstlane(
+                                            a.block_tables[(size_t)b * a.max_blocks + n]);
         if (r == 0) {  // lanes 0 .. L-1: one 16-byte column of the row each
             const size_t dst =
                 (((size_t)blk * a.num_kv_heads + g) * kBlockTokens + new_pos % kBlockTokens) * D +
@@ -449,7 +463,6 @@ struct WaveDecoder {
             *reinterpret_cast<u32x4 *>((T *)const_cast<void *>(a.k_cache) + dst) = knew;
             *reinterpret_cast<u32x4 *>((T *)const_cast<void *>(a.v_cache) + dst) = vnew;
         }
-        wait_vector_memory();
     }
 
     // Reduce the piece's per-lane state to per-head totals: afterwards every
