@@ -679,15 +679,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
 
     WaveDecoder<T, O, D, G> w(a, p_lds[wave]);
 
-    // First sequence whose units reach past u_begin.
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (__builtin_amdgcn_readfirstlane(unit_end[mid]) <= u_begin)
-            lo = mid + 1;
-        else
-            hi = mid;
-    }
+    // First sequence whose units reach past u_begin (unit_end is
+    // non-decreasing and its last entry, total, exceeds u_begin): two
+    // ballots over the wave instead of a binary search of dependent LDS
+    // reads.  Lane i first tests the last entry of group i of `step`
+    // sequences; then lane j tests entry j of the first group that reaches
+    // past u_begin.
+    const int step = (B + 63) / 64;
+    const int grp = __builtin_ctzll(__builtin_amdgcn_ballot_w64(
+        lane * step < B && unit_end[min(B - 1, lane * step + step - 1)] > u_begin));
+    const int lo = grp * step + __builtin_ctzll(__builtin_amdgcn_ballot_w64(
+        lane < step && grp * step + lane < B && unit_end[grp * step + lane] > u_begin));
     int b = lo;
     int u = u_begin;
     // A first piece that ends inside the slice leaves its arrival pending:
