@@ -453,7 +453,11 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     constexpr int NW = QD * EB / 4;        // dwords per lane per row part
     constexpr int MT = D / 16;             // 16-wide output column tiles
     constexpr int VS = kTile + 4;          // LDS row stride of a transposed V tile (elements)
-    constexpr int VT_BYTES = D * VS * EB;  // one wave's transposed V tile
+    // One wave's V tile: transposed (D x 16, row stride VS) for fp32;
+    // row-major (16 x D, row stride VRS) for 16-bit, read back through the
+    // transposing LDS read.
+    constexpr int VRS = D + 16 / EB;
+    constexpr int VT_BYTES = EB == 4 ? D * VS * EB : kTile * VRS * EB;
     constexpr int OB_BYTES = kTile * D * 4;
     constexpr int SMEM = (kMqWaves * VT_BYTES > kMqWaves * OB_BYTES) ? kMqWaves * VT_BYTES
                                                                      : kMqWaves * OB_BYTES;
@@ -540,26 +544,28 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     // Scores, softmax update and P.V of block n from its loaded K and V.
     auto compute_block = [&](int n, const uint32_t (&kw)[NW], const uint32_t (&vw)[NW]) {
         const f32x4 sc = TS::scores(kw, qw);
-        // V^T into LDS: element (d, token lr) of this lane's quarter.
+        if constexpr (EB == 4) {
+            // V^T into LDS: element (d, token lr) of this lane's quarter.
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            if constexpr (EB == 4) {
+            for (int w = 0; w < NW; ++w)
                 vt[(gq * QD + w) * VS + lr] = __builtin_bit_cast(T, vw[w]);
-            } else {
-                typedef T t2 __attribute__((ext_vector_type(2)));
-                const uint32_t word = vw[w];
-                const t2 pair = __builtin_bit_cast(t2, word);
-                vt[(gq * QD + 2 * w) * VS + lr] = pair[0];
-                vt[(gq * QD + 2 * w + 1) * VS + lr] = pair[1];
-            }
+        } else {
+            // V row lr, this lane's quarter, as it is (16-byte stores).
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                *reinterpret_cast<u32x4 *>(&vt[lr * VRS + gq * QD + 8 * i]) =
+                    u32x4{vw[4 * i], vw[4 * i + 1], vw[4 * i + 2], vw[4 * i + 3]};
         }
         float p[1][4];
         const f32x4 sv[1] = {sc};
         const bool live[1] = {true};
         st.template update<1>(sv, live, (n + 1) * kTile - 1 <= tile_first_pos, n, row_ok, my_pos,
                               a.qscale, gq, p);
-        wave_sync();  // the transposed V tile is complete
-        st.pv(vt, lr, gq, p[0]);
+        wave_sync();  // the V tile is complete
+        if constexpr (EB == 4)
+            st.pv(vt, lr, gq, p[0]);
+        else
+            st.pv_rows(vt, VRS, lr, gq, p[0]);
         wave_sync();  // reads of the V tile are done before the next block overwrites it
     };
 
