@@ -385,6 +385,32 @@ def test_fused_step_ragged_batch_and_partitions(pa, part):
     assert (got[0] == 0).all() and (got[8] == 0).all()
 
 
+@pytest.mark.parametrize("dtype", [np.float32, di.BF16])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_step_every_group(pa, dtype, group, d):
+    # up to four query heads per KV head a wave keeps two chunks in flight,
+    # with eight one; pieces of one, two and many chunks append the new row
+    rng = np.random.default_rng(32 + group + d)
+    ctx = [1, 17, 40, 65, 700, 2, 129, 31, 0, 300]
+    hkv = 2
+    q, kc, vc, tables, ctx = random_case(rng, dtype, 0, hkv * group, hkv, d, ctx_list=ctx, spare=4)
+    kn = di.cast(rng.standard_normal((len(ctx), hkv, d)), dtype)
+    vn = di.cast(rng.standard_normal((len(ctx), hkv, d)), dtype)
+    slots = derived_slots(tables, ctx)
+    ek, ev = oracle.kv_cache_write(kn, vn, slots, kc, vc)
+    ref = oracle.paged_attn_decode(q, ek, ev, tables, ctx, 0.09)
+    gk, gv = dev(kc), dev(vc)
+    for part in (0, 64):
+        gk.copy_(dev(kc))
+        gv.copy_(dev(vc))
+        out = pa.paged_attn_decode_step(dev(q), dev(kn), dev(vn), gk, gv, dev(tables), dev(ctx), 0.09,
+                                        max_context_len=int(ctx.max()), partition_tokens=part)
+        torch.cuda.synchronize()
+        assert host(gk).tobytes() == ek.tobytes() and host(gv).tobytes() == ev.tobytes()
+        assert_close(host(out), ref, dtype, f"G{group} d{d} partition {part}")
+
+
 def test_fused_step_graph_replays_match_eager(pa):
     cfg = di.CONFIGS["cb_b64"]
     lay = di.make_layout(cfg)
