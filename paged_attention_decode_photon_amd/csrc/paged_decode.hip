@@ -16,10 +16,11 @@
 // [s U_tot / NW, (s+1) U_tot / NW) (so no slice is empty and none is
 // shorter than about five units): every wave gets the same number of bytes
 // to read however ragged the contexts are, which keeps all compute units
-// streaming until the end.  Context
-// lengths live on the device, so each workgroup first forms the prefix sum
-// of per-sequence unit counts in LDS and every wave finds its first unit by
-// binary search.
+// streaming until the end.  Context lengths live on the device, so each
+// workgroup first forms the prefix sum of per-sequence unit counts in LDS
+// and every wave finds its first sequence with two wave-wide ballots.
+// Each wave keeps two chunks in flight (up to four query heads per KV head;
+// with eight the second register set would cost occupancy).
 //
 // A wave's slice covers pieces of one or more segments.  A piece that holds
 // a whole segment writes its normalised output directly.  Otherwise the
@@ -30,9 +31,10 @@
 // zero.  Waves of one segment may run on different XCDs, whose L2 caches are
 // not coherent with each other; rather than agent-scope fences (an L2
 // write-back or invalidate, far too slow here) only the partial results
-// travel coherently, as agent-scope atomic stores and loads, and a wave waits
-// for its stores to complete before it counts its arrival.  No workgroup
-// barrier is used after the prefix sum: waves never wait for each other.
+// travel coherently, as device-scope (sc1) stores and loads, and a wave's
+// stores complete before it counts its arrival with an agent-scope atomic.
+// No workgroup barrier is used after the prefix sum: waves never wait for
+// each other.
 //
 // Lane layout.  A K/V row is RB = D * sizeof(T) bytes, i.e. L = RB / 16
 // lanes of one 16-byte load each; one wave-wide load covers RPI = 64 / L
@@ -147,7 +149,7 @@ __device__ __forceinline__ void reduce_scatter(float (&part)[NS])
 
 struct KernelArgs {
     const void *q;
-    const void *k_cache;  // written only by the fused decode step (append_new_token)
+    const void *k_cache;  // written only by the fused decode step (store_new_token)
     const void *v_cache;
     const void *k_new;    // fused decode step: [B][Hkv][D] rows to append; NULL otherwise
     const void *v_new;
@@ -262,16 +264,16 @@ struct WaveDecoder {
     }
 
     // Issue the K and V loads of chunk ch (U blocks) of the current segment.
-    // With live == false every load gets an empty descriptor: it returns
+    // A block past the context gets an empty descriptor: its loads return
     // zeros without touching memory.
-    __device__ void load_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU], bool live = true) const
+    __device__ void load_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU]) const
     {
         const size_t tile_stride = (size_t)kBlockTokens * RB;
         __amdgpu_buffer_rsrc_t rk[S::U], rv[S::U];
 #pragma unroll
         for (int u = 0; u < S::U; ++u) {
             const int n = ch * S::U + u;
-            int rows = live ? ctx - n * kBlockTokens : 0;
+            int rows = ctx - n * kBlockTokens;
             rows = rows > kBlockTokens ? kBlockTokens : rows;
             int blk = 0;
             if (rows > 0)
