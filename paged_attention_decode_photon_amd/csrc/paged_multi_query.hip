@@ -14,8 +14,10 @@
 // are ordered token-major (row = j * G + head offset) and cut into tiles of
 // 16 rows.  A tile's causal range of KV blocks is cut into splits of
 // split_blocks blocks (grid z); a workgroup of four waves takes one split of
-// one tile, each wave taking every fourth block, and the four partial
-// softmax states are merged through LDS.  A tile with one split writes its
+// one tile, each wave taking every fourth block with two in flight, and the
+// four partial softmax states are merged through LDS.  (Long query runs use
+// the wide variant below: four tiles per workgroup sharing each K/V block.)
+// A tile with one split writes its
 // rows directly.  Otherwise each workgroup stores its (max, sum, unnormalised
 // rows) record with device-scope stores, waits for them, and counts its
 // arrival on the tile's counter; the workgroup that completes the count
@@ -24,17 +26,19 @@
 // they are written and read with device-scope (sc1) buffer accesses rather
 // than behind cache-wide fences.
 //
-// Matrix-core mapping (16x16 MFMA, K = 16 for 16-bit storage, K = 4 for
-// fp32).  Per KV block the wave forms S^T = K Q^T (16 tokens x 16 rows):
-// lane l supplies token l % 16 of K and row l % 16 of Q, both over the same
-// quarter D/4 * (l / 16) .. of the head dimension, since a contraction may
-// visit the head dimension in any order as long as both operands agree;
-// each lane then holds S^T[4 (l/16) + i][l % 16], i.e. four tokens of its
-// own row, which is exactly the B-operand layout of O^T = V^T P^T.  V is
-// transposed through a per-wave LDS tile so that each lane reads four
-// consecutive tokens of one column.  For 16-bit storage P is split into a
-// rounded part and its rounding residual (two MFMAs), which keeps the
-// weights as accurate as fp32.  Masked tokens (past a row's position, or
+// Matrix-core mapping (16x16 MFMA: K = 4 for fp32; K = 16 or, in the wide
+// variant and for P.V, K = 32 for 16-bit storage).  Per KV block the wave
+// forms S^T = K Q^T (16 tokens x 16 rows): lane l supplies token l % 16 of K
+// and row l % 16 of Q, both over the same quarter D/4 * (l / 16) .. of the
+// head dimension, since a contraction may visit the head dimension in any
+// order as long as both operands agree; each lane then holds
+// S^T[4 (l/16) + i][l % 16], i.e. four tokens of its own row, which is
+// exactly the B-operand layout of O^T = V^T P^T.  The V^T operand (four
+// consecutive tokens of one column per lane) comes from an LDS tile: fp32 V
+// is stored transposed, 16-bit V row-major and read back with the gfx950
+// transposing read.  For 16-bit storage P is split into a rounded part and
+// its rounding residual, which keeps the weights as accurate as fp32.
+// Masked tokens (past a row's position, or
 // past the context in the last block) get -inf scores and zero K/V rows
 // (raw buffer loads past the valid rows return zero), so pool padding never
 // reaches the arithmetic.
@@ -393,31 +397,17 @@ struct TileState {
             o_acc[t] = mfma32<T>(va[t], bl, o_acc[t]);
     }
 
-    // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS.
+    // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS (fp32
+    // storage; 16-bit V goes through pv_rows / pv_rows2).
     __device__ void pv(const T *vt, int lr, int gq, const float (&p)[4])
     {
-        if constexpr (EB == 4) {
+        static_assert(EB == 4, "16-bit V is read through the transposing LDS read");
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const f32x4 va = *reinterpret_cast<const f32x4 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], p[i], o_acc[t], 0, 0, 0);
-            }
-        } else {
-            const u32x2 p_hi = round4<T>(p);
-            float hi[4], lo[4];
-            widen4<T>(p_hi, hi);
+        for (int t = 0; t < MT; ++t) {
+            const f32x4 va = *reinterpret_cast<const f32x4 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                lo[i] = p[i] - hi[i];
-            const u32x2 p_lo = round4<T>(lo);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const u32x2 va = *reinterpret_cast<const u32x2 *>(&vt[(16 * t + lr) * VS + 4 * gq]);
-                o_acc[t] = mfma16<T>(va, p_hi, o_acc[t]);
-                o_acc[t] = mfma16<T>(va, p_lo, o_acc[t]);
-            }
+                o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], p[i], o_acc[t], 0, 0, 0);
         }
     }
 };
