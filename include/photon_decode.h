@@ -105,7 +105,8 @@ typedef struct photon_decode_desc {
                                    actual batch is always split evenly over
                                    the wavefronts this implies, but over no
                                    more than one per five quanta of it (a
-                                   slice is never much shorter than five)      */
+                                   slice is never much shorter than five)
+                                   unless that leaves fewer than 256          */
     photon_kv_desc kv;
     int32_t flags;              /* PHOTON_DECODE_* bits, 0 = none; other bits
                                    are PHOTON_ERR_INVALID_ARG                    */

@@ -12,9 +12,10 @@
 // so every K/V byte is fetched from HBM once.  A segment is cut into chunks
 // of CT = 16 U tokens; the chunks of all segments, sequence-major then
 // KV-head-major, form one list of U_tot units.  Of the wavefronts launched,
-// NW = min(launched, ceil(U_tot / 5)) take part, and wave s takes units
-// [s U_tot / NW, (s+1) U_tot / NW) (so no slice is empty and none is
-// shorter than about five units): every wave gets the same number of bytes
+// NW = min(launched, max(ceil(U_tot / 5), min(U_tot, 256))) take part, and
+// wave s takes units [s U_tot / NW, (s+1) U_tot / NW) (so no slice is empty,
+// and none is shorter than about five units unless the call is small):
+// every wave gets the same number of bytes
 // to read however ragged the contexts are, which keeps all compute units
 // streaming until the end.  Context lengths live on the device, so each
 // workgroup first forms the prefix sum of per-sequence unit counts in LDS
@@ -75,10 +76,14 @@ namespace {
 
 // Fourth descriptor word of a raw (unswizzled, stride 0) buffer on gfx9-family.
 constexpr int kRawBufferWord3 = 0x00020000;
-// Fewest units a wavefront's slice holds (unless the whole call has fewer):
-// measured best among 1-6 on the batch-16 (fp32 and bf16), ragged batch-64
-// and long-context workloads.
+// Fewest units a wavefront's slice holds while more than kMinWaves waves
+// would take part: measured best among 1-6 on the batch-16 (fp32 and bf16),
+// ragged batch-64 and long-context workloads.  Small calls keep kMinWaves
+// waves (one per CU), since there the latency of a wave's chain of chunks
+// dominates: batch 1 at 512 tokens takes 10.5 us with one unit per wave
+// against 14.3 us with five.
 constexpr int kMinUnitsPerWave = 5;
+constexpr int kMinWaves = 256;
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -667,13 +672,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
                 row[i] = Elem<O>::from_float(0.0f);
         }
     }
-    // At most one wavefront per kMinUnitsPerWave units: a wave's fixed costs
-    // (prefix, first table window and round trip, record, arrival, merge)
-    // are paid once per slice, and fewer, longer slices also mean fewer
-    // records and arrivals per segment.  The slices are never empty, so
-    // every slice between two others holds a record of any segment
-    // spanning them.
-    const int nw = min(a.num_waves, (total + kMinUnitsPerWave - 1) / kMinUnitsPerWave);
+    // At most one wavefront per kMinUnitsPerWave units, but no fewer than
+    // kMinWaves (or one per unit): a wave's fixed costs (prefix, first table
+    // window and round trip, record, arrival, merge) are paid once per
+    // slice, and fewer, longer slices also mean fewer records and arrivals
+    // per segment, until too few waves are left to hide memory latency.
+    // The slices are never empty, so every slice between two others holds a
+    // record of any segment spanning them.
+    const int nw = min(a.num_waves, max((total + kMinUnitsPerWave - 1) / kMinUnitsPerWave,
+                                        min(total, kMinWaves)));
     if (s >= nw)
         return;
     const int u_begin = slice_start(s, total, nw);
