@@ -371,7 +371,9 @@ def serving_measurements(cfg, device, stream, trace_name: str = "serving"):
     decode kernel when every sequence has one new token.  q/k/v of
     the new tokens are synthetic (no model).  Reported: attention-path GPU
     time per step (events around the two launches) and new tokens per
-    second, over all steps and over the decode-only steps.
+    second, over all steps and over the decode-only steps.  Each step's
+    launches are enqueued behind a short GPU sleep, so the events time the
+    kernels back to back rather than the host's launch overhead between them.
     """
     import paged_attention_decode_photon_amd as pa
     import torch
@@ -405,6 +407,16 @@ def serving_measurements(cfg, device, stream, trace_name: str = "serving"):
     def event():
         return torch.cuda.Event(enable_timing=True)
 
+    # cycles of torch.cuda._sleep per microsecond, to hold the GPU about
+    # 200 us while a step's launches are enqueued
+    torch.cuda.synchronize()
+    c0, c1 = event(), event()
+    c0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    hold_cycles = int(1_000_000 * 200.0 / max(c0.elapsed_time(c1) * 1e3, 1.0))
+
     records = []
     i, done, step = 0, 0, 0
     torch.cuda.synchronize()
@@ -431,6 +443,7 @@ def serving_measurements(cfg, device, stream, trace_name: str = "serving"):
             if need > ws.numel():
                 ws = pa.new_workspace(need, device)
             e0, e1 = event(), event()
+            torch.cuda._sleep(hold_cycles)
             e0.record(stream)
             pa.rope_kv_cache_write(q[:t], k[:t], v[:t], devb["pos"][:t], devb["slot"][:t], kc, vc,
                                    cfg.rope_base, q_out=qr[:t])
