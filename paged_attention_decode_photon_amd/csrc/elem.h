@@ -59,6 +59,13 @@ struct Elem<_Float16> {
         return v;
     }
     __device__ static _Float16 from_float(float x) { return (_Float16)x; }
+    // acc + x.lo * y.lo + x.hi * y.hi over two packed elements, in fp32
+    // (v_dot2_f32_f16; the products of two halves are exact in fp32).
+    __device__ static float dot2(uint32_t x, uint32_t y, float acc)
+    {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x),
+                                      __builtin_bit_cast(half2_t, y), acc, false);
+    }
 };
 
 // bfloat16 is the upper half of a binary32, so widening is a shift; narrowing
@@ -88,6 +95,12 @@ struct Elem<__bf16> {
         return v;
     }
     __device__ static __bf16 from_float(float x) { return (__bf16)x; }
+    // acc + x.lo * y.lo + x.hi * y.hi in fp32 (v_dot2_f32_bf16).
+    __device__ static float dot2(uint32_t x, uint32_t y, float acc)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, x),
+                                               __builtin_bit_cast(bf162_t, y), acc, false);
+    }
 };
 
 // Store E consecutive outputs of type O (E * sizeof(O) is 16 or 32 bytes).

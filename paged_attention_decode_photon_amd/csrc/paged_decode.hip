@@ -60,9 +60,15 @@
 // blocks past it return zero without touching memory, and their scores are
 // set to -inf, so pool padding (even NaN) never reaches the arithmetic.
 //
-// Softmax.  Scores are kept in log2 units (q is pre-multiplied by
-// scale * log2 e) and use v_exp_f32.  Each wave keeps an online maximum and
-// sum per head over its piece.
+// Dot products.  fp32 rows: q is widened once per piece, pre-multiplied by
+// scale * log2 e, and each partial product is a chain of FMAs.  16-bit rows:
+// q stays packed and K is never widened; each partial product is a chain of
+// two-element dot instructions (v_dot2_f32_f16 / v_dot2_f32_bf16, fp32
+// accumulation), half the instructions and no conversions, and the reduced
+// score is multiplied by scale * log2 e.
+//
+// Softmax.  Scores are kept in log2 units and use v_exp_f32.  Each wave
+// keeps an online maximum and sum per head over its piece.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -201,7 +207,13 @@ struct WaveDecoder {
     int nblk;      // blocks holding the sequence's context
     int win0;      // first block index of the table window
     int tbl_win;   // lane i: block_tables[b][win0 + i] (0 past the context)
+    // Query rows of the piece, this lane's chunk of each head.  fp32 storage:
+    // widened and pre-multiplied by the scale (qf).  16-bit storage: kept
+    // packed (qpk) for two-element dot instructions; the scale then goes on
+    // the reduced score.
+    static constexpr bool kPackedQ = S::EB == 2;
     float qf[G][E];
+    u32x4 qpk[G];
     float m_run, l_run;
     float o_acc[G][E];
 
@@ -253,10 +265,14 @@ struct WaveDecoder {
 #pragma unroll
         for (int hs = 0; hs < G; ++hs) {
             const T *row = q + ((size_t)b * hq + (size_t)g * G + (hs ^ head_x)) * D + c * E;
-            Elem<T>::unpack(*reinterpret_cast<const u32x4 *>(row), qf[hs]);
+            if constexpr (kPackedQ) {
+                qpk[hs] = *reinterpret_cast<const u32x4 *>(row);
+            } else {
+                Elem<T>::unpack(*reinterpret_cast<const u32x4 *>(row), qf[hs]);
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                qf[hs][e] *= a.qscale;
+                for (int e = 0; e < E; ++e)
+                    qf[hs][e] *= a.qscale;
+            }
         }
         new_pos = -1;
         m_run = -INFINITY;
@@ -314,15 +330,31 @@ struct WaveDecoder {
         float part[NS];
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
-            float kf[E];
-            Elem<T>::unpack(kd[i], kf);
+            if constexpr (kPackedQ) {
 #pragma unroll
-            for (int hs = 0; hs < G; ++hs) {
-                float acc = 0.0f;
+                for (int hs = 0; hs < G; ++hs) {
+                    float acc = 0.0f;
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    acc = __builtin_fmaf(qf[hs][e], kf[e], acc);
-                part[i * G + hs] = acc;
+                    for (int w = 0; w < 4; ++w) {
+                        // Copy the dwords out of the vectors before the bit
+                        // cast inside dot2 (see Elem<_Float16>::unpack).
+                        const uint32_t qw = qpk[hs][w];
+                        const uint32_t kw = kd[i][w];
+                        acc = Elem<T>::dot2(qw, kw, acc);
+                    }
+                    part[i * G + hs] = acc;
+                }
+            } else {
+                float kf[E];
+                Elem<T>::unpack(kd[i], kf);
+#pragma unroll
+                for (int hs = 0; hs < G; ++hs) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        acc = __builtin_fmaf(qf[hs][e], kf[e], acc);
+                    part[i * G + hs] = acc;
+                }
             }
         }
         reduce_scatter<NS, CP, CP - 1>(part);
@@ -335,6 +367,8 @@ struct WaveDecoder {
 #pragma unroll
         for (int n = 0; n < NK; ++n) {
             float v = allreduce_bits<CP, S::LOG2L, OpSum>(part[n << CP]);
+            if constexpr (kPackedQ)
+                v *= a.qscale;
             const int item = (n << CP) | phi;
             const int ld = item >> S::LOG2G;
             const int tok = (ld / NIB) * kBlockTokens + (ld % NIB) * RPI + r;
