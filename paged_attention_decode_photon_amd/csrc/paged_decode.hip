@@ -12,14 +12,16 @@
 // so every K/V byte is fetched from HBM once.  A segment is cut into chunks
 // of CT = 16 U tokens; the chunks of all segments, sequence-major then
 // KV-head-major, form one list of U_tot units.  Of the wavefronts launched,
-// NW = min(launched, max(ceil(U_tot / 5), min(U_tot, 256))) take part, and
-// wave s takes units [s U_tot / NW, (s+1) U_tot / NW) (so no slice is empty,
-// and none is shorter than about five units unless the call is small):
-// every wave gets the same number of bytes
-// to read however ragged the contexts are, which keeps all compute units
-// streaming until the end.  Context lengths live on the device, so each
-// workgroup first forms the prefix sum of per-sequence unit counts in LDS
-// and every wave finds its first sequence with two wave-wide ballots.
+// NW = min(launched, max(ceil(U_tot / 5), min(U_tot, 256))) take part.  In
+// the list they split, each non-empty segment is preceded by C empty
+// entries (C = 2 once slices hold five units or more, else 0), and wave s
+// takes entries [s L / NW, (s+1) L / NW) of its L entries: every wave gets
+// the same amount of work however ragged the contexts are, a slice that
+// changes segment being charged two units for it, which keeps all compute
+// units busy until the end.  Context lengths live on the device, so each
+// workgroup first forms the prefix sums of per-sequence unit counts and of
+// non-empty sequences in LDS, and every wave finds its first sequence with
+// two wave-wide ballots.
 // Each wave keeps two chunks in flight (up to four query heads per KV head;
 // with eight the second register set would cost occupancy).
 //
@@ -90,6 +92,13 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // against 14.3 us with five.
 constexpr int kMinUnitsPerWave = 5;
 constexpr int kMinWaves = 256;
+// Work a wavefront is charged for starting on a segment, in units: a piece
+// change costs a record, an arrival and a fresh first round trip, so when
+// slices hold kMinUnitsPerWave units or more, each non-empty segment is
+// counted as this many units longer (empty units at its start).  A slice
+// that spans a segment change then holds that many fewer chunks.  Two was
+// measured best among one to three (ragged batch-64: 29.6 -> 28.2 us).
+constexpr int kBoundaryUnits = 2;
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -572,12 +581,15 @@ struct WaveDecoder {
     // Merge the records of every piece of segment (sb, sg), units [su0, su1),
     // in slice order, and write the normalised output.  Each lane folds four
     // consecutive outputs of one head; kBatch records are loaded at a time.
-    __device__ void merge_segment(int sb, int sg, int su0, int su1, int total, int nw) const
+    // The segment's units are [su0, su1) of the slice list, after its empty
+    // units, which start at sv0: a slice that starts at or after sv0 has this
+    // segment as its first piece.
+    __device__ void merge_segment(int sb, int sg, int sv0, int su0, int su1, int total, int nw) const
     {
         constexpr int kBatch = 8;
         const int s_first = slice_of(su0, total, nw);
         const int s_last = slice_of(su1 - 1, total, nw);
-        const int first_role = slice_start(s_first, total, nw) == su0 ? 0 : 1;
+        const int first_role = slice_start(s_first, total, nw) >= sv0 ? 0 : 1;
         O *dst = out_rows(sb, sg);
         compiler_memory_barrier();
         for (int v = lane; v < G * D / 4; v += 64) {
@@ -629,25 +641,30 @@ struct WaveDecoder {
     }
 };
 
-// Inclusive prefix sum of one value per thread over the workgroup.
-__device__ int block_inclusive_scan(int v, int *wave_totals)
+// Inclusive prefix sums of two values per thread over the workgroup.
+__device__ int2 block_inclusive_scan2(int2 v, int2 *wave_totals)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int n = __shfl_up(v, d, 64);
-        if (lane >= d)
-            v += n;
+        const int nx = __shfl_up(v.x, d, 64);
+        const int ny = __shfl_up(v.y, d, 64);
+        if (lane >= d) {
+            v.x += nx;
+            v.y += ny;
+        }
     }
     if (lane == 63)
         wave_totals[wave] = v;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w)
-        before += wave_totals[w];
+    int2 before = make_int2(0, 0);
+    for (int w = 0; w < wave; ++w) {
+        before.x += wave_totals[w].x;
+        before.y += wave_totals[w].y;
+    }
     __syncthreads();
-    return v + before;
+    return make_int2(v.x + before.x, v.y + before.y);
 }
 
 template <typename T, typename O, int D, int G>
@@ -659,32 +676,39 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     constexpr int NT = WAVES * 64;
 
     __shared__ int unit_end[kMaxDecodeSeqs];  // inclusive prefix of units per sequence
+    __shared__ int ne_end[kMaxDecodeSeqs];    // inclusive count of non-empty sequences
     __shared__ int ctx_lds[kMaxDecodeSeqs];
-    __shared__ int wave_totals[WAVES];
+    __shared__ int2 wave_totals[WAVES];
     __shared__ __attribute__((aligned(16))) float p_lds[WAVES][CT][G];
 
     const int B = a.num_seqs;
     const int hkv = a.num_kv_heads;
 
-    // Units per sequence (Hkv * chunks) and their inclusive prefix sum.  Each
-    // thread owns a contiguous run of sequences.
+    // Units per sequence (Hkv * chunks) and non-empty sequences, with their
+    // inclusive prefix sums.  Each thread owns a contiguous run of sequences.
     const int per = (B + NT - 1) / NT;
     const int first = threadIdx.x * per;
-    int mine = 0;
+    int2 mine = make_int2(0, 0);
     for (int j = 0; j < per; ++j) {
         const int bb = first + j;
         if (bb < B) {
             const int cl = a.context_lens[bb];
             ctx_lds[bb] = cl;
-            mine += hkv * ((cl + CT - 1) / CT);
+            mine.x += hkv * ((cl + CT - 1) / CT);
+            mine.y += cl > 0 ? 1 : 0;
         }
     }
-    int run = block_inclusive_scan(mine, wave_totals) - mine;
+    int2 run = block_inclusive_scan2(mine, wave_totals);
+    run.x -= mine.x;
+    run.y -= mine.y;
     for (int j = 0; j < per; ++j) {
         const int bb = first + j;
         if (bb < B) {
-            run += hkv * ((ctx_lds[bb] + CT - 1) / CT);
-            unit_end[bb] = run;
+            const int cl = ctx_lds[bb];
+            run.x += hkv * ((cl + CT - 1) / CT);
+            run.y += cl > 0 ? 1 : 0;
+            unit_end[bb] = run.x;
+            ne_end[bb] = run.y;
         }
     }
     __syncthreads();
@@ -711,30 +735,37 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     // window and round trip, record, arrival, merge) are paid once per
     // slice, and fewer, longer slices also mean fewer records and arrivals
     // per segment, until too few waves are left to hide memory latency.
-    // The slices are never empty, so every slice between two others holds a
-    // record of any segment spanning them.
     const int nw = min(a.num_waves, max((total + kMinUnitsPerWave - 1) / kMinUnitsPerWave,
                                         min(total, kMinWaves)));
     if (s >= nw)
         return;
-    const int u_begin = slice_start(s, total, nw);
-    const int u_end = slice_start(s + 1, total, nw);
+    // Slices split the list in which every non-empty segment starts with C
+    // empty units (none for small calls, whose slices hold one or two
+    // units).  Slices hold at least four list entries when C > 0, so every
+    // slice holds work, and every slice between two others holds a record
+    // of any segment spanning them.
+    const int C = total >= kMinUnitsPerWave * kMinWaves ? kBoundaryUnits : 0;
+    const int total_v = total + C * hkv * __builtin_amdgcn_readfirstlane(ne_end[B - 1]);
+    const int v_begin = slice_start(s, total_v, nw);
+    const int v_end = slice_start(s + 1, total_v, nw);
+    // End of sequence bb's entries in that list.
+    auto seq_end_of = [&](int bb) { return unit_end[bb] + C * hkv * ne_end[bb]; };
 
     WaveDecoder<T, O, D, G> w(a, p_lds[wave]);
 
-    // First sequence whose units reach past u_begin (unit_end is
-    // non-decreasing and its last entry, total, exceeds u_begin): two
-    // ballots over the wave instead of a binary search of dependent LDS
-    // reads.  Lane i first tests the last entry of group i of `step`
-    // sequences; then lane j tests entry j of the first group that reaches
-    // past u_begin.
+    // First sequence whose entries reach past v_begin (the ends are
+    // non-decreasing and the last, total_v, exceeds v_begin): two ballots
+    // over the wave instead of a binary search of dependent LDS reads.
+    // Lane i first tests the last entry of group i of `step` sequences; then
+    // lane j tests entry j of the first group that reaches past v_begin.
     const int step = (B + 63) / 64;
     const int grp = __builtin_ctzll(__builtin_amdgcn_ballot_w64(
-        lane * step < B && unit_end[min(B - 1, lane * step + step - 1)] > u_begin));
+        lane * step < B && seq_end_of(min(B - 1, lane * step + step - 1)) > v_begin));
     const int lo = grp * step + __builtin_ctzll(__builtin_amdgcn_ballot_w64(
-        lane < step && grp * step + lane < B && unit_end[grp * step + lane] > u_begin));
+        lane < step && grp * step + lane < B && seq_end_of(min(B - 1, grp * step + lane)) > v_begin));
     int b = lo;
-    int u = u_begin;
+    int v = v_begin;
+    bool first_piece = true;
     // A first piece that ends inside the slice leaves its arrival pending:
     // it is counted once the next piece's first loads are on their way, so
     // the record stores complete during that round trip instead of stalling
@@ -742,17 +773,20 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     // then, should this wave have completed the segment).
     bool pend = false, pend_count_now = false;
     int pend_b = 0, pend_g = 0, pend_seg = 0, pend_nch = 0, pend_units = 0, pend_old = 0;
-    while (u < u_end) {
-        const int seq_end = __builtin_amdgcn_readfirstlane(unit_end[b]);
+    while (true) {
+        const int seq_end = __builtin_amdgcn_readfirstlane(seq_end_of(b));
         const int ctx = __builtin_amdgcn_readfirstlane(ctx_lds[b]);
-        const int nch = (ctx + CT - 1) / CT;        // > 0: u lies inside sequence b
-        const int seq_begin = seq_end - hkv * nch;
-        const int g = (u - seq_begin) / nch;
-        const int seg_begin = seq_begin + g * nch;  // first unit of segment (b, g)
-        const int seg_end = seg_begin + nch;
-        const int piece_end = min(seg_end, u_end);
-        const int ch0 = u - seg_begin;
-        const int ch1 = piece_end - seg_begin;
+        const int nch = (ctx + CT - 1) / CT;  // > 0: v lies inside sequence b
+        const int stride = nch + C;           // list entries per segment
+        const int seq_begin = seq_end - hkv * stride;
+        const int g = (v - seq_begin) / stride;
+        const int seg_v0 = seq_begin + g * stride;  // first entry of segment (b, g)
+        const int r0 = max(v, seg_v0 + C);
+        if (r0 >= v_end)  // only empty units left in this slice
+            break;
+        const int r1 = min(v_end, seg_v0 + stride);
+        const int ch0 = r0 - seg_v0 - C;
+        const int ch1 = r1 - seg_v0 - C;
 
         w.begin_piece(b, g, ctx, ch0);
         const bool appends = a.k_new != nullptr && ch1 == nch;
@@ -774,13 +808,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         if (ch0 == 0 && ch1 == nch) {
             w.write_output();
         } else {
-            const int role = (u == u_begin) ? 0 : 1;
+            const int role = first_piece ? 0 : 1;
             w.store_record(a.ws_rec + ((size_t)s * 2 + role) * S::REC);
-            if (piece_end < u_end) {  // only a slice's first piece ends early
+            if (first_piece && r1 + C < v_end) {  // another piece follows in this slice
                 pend = pend_count_now = true;
                 pend_b = b;
                 pend_g = g;
-                pend_seg = seg_begin;
+                pend_seg = seg_v0;
                 pend_nch = nch;
                 pend_units = ch1 - ch0;
             } else {
@@ -791,22 +825,26 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 done = __builtin_amdgcn_readfirstlane(done) + (ch1 - ch0);
                 if (done == nch) {
-                    w.merge_segment(b, g, seg_begin, seg_end, total, nw);
+                    w.merge_segment(b, g, seg_v0, seg_v0 + C, seg_v0 + stride, total_v, nw);
                     if (lane == 0)
                         __hip_atomic_store(&a.ws_count[(size_t)b * hkv + g], 0, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
-        u = piece_end;
-        if (u == seq_end) {  // move on to the next sequence that has units
+        first_piece = false;
+        v = r1;
+        if (v >= v_end)
+            break;
+        if (v == seq_end) {  // move on to the next sequence that has units
             ++b;
-            while (b < B && __builtin_amdgcn_readfirstlane(unit_end[b]) == u)
+            while (b < B && __builtin_amdgcn_readfirstlane(unit_end[b]) ==
+                                __builtin_amdgcn_readfirstlane(unit_end[b - 1]))
                 ++b;
         }
     }
     if (pend && __builtin_amdgcn_readfirstlane(pend_old) + pend_units == pend_nch) {
-        w.merge_segment(pend_b, pend_g, pend_seg, pend_seg + pend_nch, total, nw);
+        w.merge_segment(pend_b, pend_g, pend_seg, pend_seg + C, pend_seg + C + pend_nch, total_v, nw);
         if (lane == 0)
             __hip_atomic_store(&a.ws_count[(size_t)pend_b * hkv + pend_g], 0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
