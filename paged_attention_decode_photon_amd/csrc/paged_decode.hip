@@ -11,11 +11,11 @@
 // (sequence b, KV head g) pair together with the G query heads that read it,
 // so every K/V byte is fetched from HBM once.  A segment is cut into chunks
 // of CT = 16 U tokens; the chunks of all segments, sequence-major then
-// KV-head-major, form one list of U_tot units.  Of the wavefronts launched,
-// NW = min(launched, max(ceil(U_tot / 5), min(U_tot, 256))) take part.  In
-// the list they split, each non-empty segment is preceded by C empty
-// entries (C = 2 once slices hold five units or more, else 0), and wave s
-// takes entries [s L / NW, (s+1) L / NW) of its L entries: every wave gets
+// KV-head-major, form one list of U_tot units.  In the list the waves
+// split, each non-empty segment is preceded by C empty entries (C = 2 once
+// slices hold five units or more, else 0); of the wavefronts launched,
+// NW = min(launched, max(ceil(L / 5), min(U_tot, 256))) take part, for L
+// list entries, and wave s takes entries [s L / NW, (s+1) L / NW): every wave gets
 // the same amount of work however ragged the contexts are, a slice that
 // changes segment being charged two units for it, which keeps all compute
 // units busy until the end.  Context lengths live on the device, so each
@@ -730,22 +730,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
                 row[i] = Elem<O>::from_float(0.0f);
         }
     }
-    // At most one wavefront per kMinUnitsPerWave units, but no fewer than
-    // kMinWaves (or one per unit): a wave's fixed costs (prefix, first table
-    // window and round trip, record, arrival, merge) are paid once per
-    // slice, and fewer, longer slices also mean fewer records and arrivals
-    // per segment, until too few waves are left to hide memory latency.
-    const int nw = min(a.num_waves, max((total + kMinUnitsPerWave - 1) / kMinUnitsPerWave,
+    // Slices split the list in which every non-empty segment starts with C
+    // empty units (none for small calls, whose slices hold one or two
+    // units).  At most one wavefront per kMinUnitsPerWave entries of that
+    // list, but no fewer than kMinWaves (or one per unit): a wave's fixed
+    // costs (prefix, first table window and round trip, record, arrival,
+    // merge) are paid once per slice, and fewer, longer slices also mean
+    // fewer records and arrivals per segment, until too few waves are left
+    // to hide memory latency.  Slices hold at least four list entries when
+    // C > 0, so every slice holds work, and every slice between two others
+    // holds a record of any segment spanning them.
+    const int C = total >= kMinUnitsPerWave * kMinWaves ? kBoundaryUnits : 0;
+    const int total_v = total + C * hkv * __builtin_amdgcn_readfirstlane(ne_end[B - 1]);
+    const int nw = min(a.num_waves, max((total_v + kMinUnitsPerWave - 1) / kMinUnitsPerWave,
                                         min(total, kMinWaves)));
     if (s >= nw)
         return;
-    // Slices split the list in which every non-empty segment starts with C
-    // empty units (none for small calls, whose slices hold one or two
-    // units).  Slices hold at least four list entries when C > 0, so every
-    // slice holds work, and every slice between two others holds a record
-    // of any segment spanning them.
-    const int C = total >= kMinUnitsPerWave * kMinWaves ? kBoundaryUnits : 0;
-    const int total_v = total + C * hkv * __builtin_amdgcn_readfirstlane(ne_end[B - 1]);
     const int v_begin = slice_start(s, total_v, nw);
     const int v_end = slice_start(s + 1, total_v, nw);
     // End of sequence bb's entries in that list.
