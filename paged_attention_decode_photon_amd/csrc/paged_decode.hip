@@ -18,10 +18,11 @@
 // list entries, and wave s takes entries [s L / NW, (s+1) L / NW): every wave gets
 // the same amount of work however ragged the contexts are, a slice that
 // changes segment being charged two units for it, which keeps all compute
-// units busy until the end.  Context lengths live on the device, so each
-// workgroup first forms the prefix sums of per-sequence unit counts and of
-// non-empty sequences in LDS, and every wave finds its first sequence with
-// two wave-wide ballots.
+// units busy until the end.  Context lengths live on the device, so the
+// kernel first forms the prefix sums of per-sequence unit counts and of
+// non-empty sequences: each wave in its own registers for up to 64
+// sequences, else each workgroup in LDS; every wave then finds its first
+// sequence with one or two wave-wide ballots.
 // Each wave keeps two chunks in flight (up to four query heads per KV head;
 // with eight the second register set would cost occupancy).
 //
@@ -684,47 +685,83 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     const int B = a.num_seqs;
     const int hkv = a.num_kv_heads;
 
-    // Units per sequence (Hkv * chunks) and non-empty sequences, with their
-    // inclusive prefix sums.  Each thread owns a contiguous run of sequences.
-    const int per = (B + NT - 1) / NT;
-    const int first = threadIdx.x * per;
-    int2 mine = make_int2(0, 0);
-    for (int j = 0; j < per; ++j) {
-        const int bb = first + j;
-        if (bb < B) {
-            const int cl = a.context_lens[bb];
-            ctx_lds[bb] = cl;
-            mine.x += hkv * ((cl + CT - 1) / CT);
-            mine.y += cl > 0 ? 1 : 0;
-        }
-    }
-    int2 run = block_inclusive_scan2(mine, wave_totals);
-    run.x -= mine.x;
-    run.y -= mine.y;
-    for (int j = 0; j < per; ++j) {
-        const int bb = first + j;
-        if (bb < B) {
-            const int cl = ctx_lds[bb];
-            run.x += hkv * ((cl + CT - 1) / CT);
-            run.y += cl > 0 ? 1 : 0;
-            unit_end[bb] = run.x;
-            ne_end[bb] = run.y;
-        }
-    }
-    __syncthreads();
-
-    // Values read from LDS are the same in every lane, but the compiler cannot
-    // know that; readfirstlane keeps everything derived from them in scalar
-    // registers (a divergent buffer descriptor would wrap each load in a
-    // waterfall loop).
-    const int total = __builtin_amdgcn_readfirstlane(unit_end[B - 1]);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Per sequence: its context length, and the inclusive prefix sums of
+    // units (Hkv * chunks) and of non-empty sequences.  Up to 64 sequences,
+    // every wave computes them for itself in registers (lane b holds
+    // sequence b; a wave-wide scan, no workgroup barrier and no LDS).  Larger
+    // batches scan over the workgroup into LDS, each thread owning a
+    // contiguous run of sequences.
     const int lane = threadIdx.x & 63;
+    const bool small = B <= 64;
+    int r_ctx = 0, r_end = 0, r_ne = 0;
+    if (small) {
+        const int cl = lane < B ? a.context_lens[lane] : 0;
+        int u = hkv * ((cl + CT - 1) / CT), n = cl > 0 ? 1 : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int nu = __shfl_up(u, d, 64);
+            const int nn = __shfl_up(n, d, 64);
+            if (lane >= d) {
+                u += nu;
+                n += nn;
+            }
+        }
+        r_ctx = cl;
+        r_end = u;
+        r_ne = n;
+    } else {
+        const int per = (B + NT - 1) / NT;
+        const int first = threadIdx.x * per;
+        int2 mine = make_int2(0, 0);
+        for (int j = 0; j < per; ++j) {
+            const int bb = first + j;
+            if (bb < B) {
+                const int cl = a.context_lens[bb];
+                ctx_lds[bb] = cl;
+                mine.x += hkv * ((cl + CT - 1) / CT);
+                mine.y += cl > 0 ? 1 : 0;
+            }
+        }
+        int2 run = block_inclusive_scan2(mine, wave_totals);
+        run.x -= mine.x;
+        run.y -= mine.y;
+        for (int j = 0; j < per; ++j) {
+            const int bb = first + j;
+            if (bb < B) {
+                const int cl = ctx_lds[bb];
+                run.x += hkv * ((cl + CT - 1) / CT);
+                run.y += cl > 0 ? 1 : 0;
+                unit_end[bb] = run.x;
+                ne_end[bb] = run.y;
+            }
+        }
+        __syncthreads();
+    }
+    // Accessors for a wave-uniform sequence index.  Values read from LDS are
+    // the same in every lane, but the compiler cannot know that;
+    // readfirstlane keeps everything derived from them in scalar registers
+    // (a divergent buffer descriptor would wrap each load in a waterfall
+    // loop).
+    auto ctx_of = [&](int bb) -> int {
+        return small ? __builtin_amdgcn_readlane(r_ctx, bb)
+                     : __builtin_amdgcn_readfirstlane(ctx_lds[bb]);
+    };
+    auto end_of = [&](int bb) -> int {
+        return small ? __builtin_amdgcn_readlane(r_end, bb)
+                     : __builtin_amdgcn_readfirstlane(unit_end[bb]);
+    };
+    auto ne_of = [&](int bb) -> int {
+        return small ? __builtin_amdgcn_readlane(r_ne, bb)
+                     : __builtin_amdgcn_readfirstlane(ne_end[bb]);
+    };
+
+    const int total = end_of(B - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = blockIdx.x * WAVES + wave;
 
     // Sequences with an empty context have no units; their rows are zero.
     for (int bb = s; bb < B; bb += a.num_waves) {
-        if (__builtin_amdgcn_readfirstlane(ctx_lds[bb]) == 0) {
+        if (ctx_of(bb) == 0) {
             O *row = (O *)a.out + (size_t)bb * hkv * G * D;
             for (int i = lane; i < hkv * G * D; i += 64)
                 row[i] = Elem<O>::from_float(0.0f);
@@ -741,29 +778,34 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     // C > 0, so every slice holds work, and every slice between two others
     // holds a record of any segment spanning them.
     const int C = total >= kMinUnitsPerWave * kMinWaves ? kBoundaryUnits : 0;
-    const int total_v = total + C * hkv * __builtin_amdgcn_readfirstlane(ne_end[B - 1]);
+    const int total_v = total + C * hkv * ne_of(B - 1);
     const int nw = min(a.num_waves, max((total_v + kMinUnitsPerWave - 1) / kMinUnitsPerWave,
                                         min(total, kMinWaves)));
     if (s >= nw)
         return;
     const int v_begin = slice_start(s, total_v, nw);
     const int v_end = slice_start(s + 1, total_v, nw);
-    // End of sequence bb's entries in that list.
-    auto seq_end_of = [&](int bb) { return unit_end[bb] + C * hkv * ne_end[bb]; };
+    // End of sequence bb's entries in that list (any lane's bb; LDS path).
+    auto seq_end_lds = [&](int bb) { return unit_end[bb] + C * hkv * ne_end[bb]; };
 
     WaveDecoder<T, O, D, G> w(a, p_lds[wave]);
 
     // First sequence whose entries reach past v_begin (the ends are
-    // non-decreasing and the last, total_v, exceeds v_begin): two ballots
-    // over the wave instead of a binary search of dependent LDS reads.
-    // Lane i first tests the last entry of group i of `step` sequences; then
-    // lane j tests entry j of the first group that reaches past v_begin.
-    const int step = (B + 63) / 64;
-    const int grp = __builtin_ctzll(__builtin_amdgcn_ballot_w64(
-        lane * step < B && seq_end_of(min(B - 1, lane * step + step - 1)) > v_begin));
-    const int lo = grp * step + __builtin_ctzll(__builtin_amdgcn_ballot_w64(
-        lane < step && grp * step + lane < B && seq_end_of(min(B - 1, grp * step + lane)) > v_begin));
-    int b = lo;
+    // non-decreasing and the last, total_v, exceeds v_begin): one ballot
+    // over the registers of a small batch; for larger ones two ballots
+    // instead of a binary search of dependent LDS reads (lane i first tests
+    // the last entry of group i of `step` sequences; then lane j tests entry
+    // j of the first group that reaches past v_begin).
+    int b;
+    if (small) {
+        b = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < B && r_end + C * hkv * r_ne > v_begin));
+    } else {
+        const int step = (B + 63) / 64;
+        const int grp = __builtin_ctzll(__builtin_amdgcn_ballot_w64(
+            lane * step < B && seq_end_lds(min(B - 1, lane * step + step - 1)) > v_begin));
+        b = grp * step + __builtin_ctzll(__builtin_amdgcn_ballot_w64(
+            lane < step && grp * step + lane < B && seq_end_lds(min(B - 1, grp * step + lane)) > v_begin));
+    }
     int v = v_begin;
     bool first_piece = true;
     // A first piece that ends inside the slice leaves its arrival pending:
@@ -774,8 +816,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     bool pend = false, pend_count_now = false;
     int pend_b = 0, pend_g = 0, pend_seg = 0, pend_nch = 0, pend_units = 0, pend_old = 0;
     while (true) {
-        const int seq_end = __builtin_amdgcn_readfirstlane(seq_end_of(b));
-        const int ctx = __builtin_amdgcn_readfirstlane(ctx_lds[b]);
+        const int seq_end = end_of(b) + C * hkv * ne_of(b);
+        const int ctx = ctx_of(b);
         const int nch = (ctx + CT - 1) / CT;  // > 0: v lies inside sequence b
         const int stride = nch + C;           // list entries per segment
         const int seq_begin = seq_end - hkv * stride;
@@ -838,8 +880,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
             break;
         if (v == seq_end) {  // move on to the next sequence that has units
             ++b;
-            while (b < B && __builtin_amdgcn_readfirstlane(unit_end[b]) ==
-                                __builtin_amdgcn_readfirstlane(unit_end[b - 1]))
+            while (b < B && end_of(b) == end_of(b - 1))
                 ++b;
         }
     }
