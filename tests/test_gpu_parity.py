@@ -476,3 +476,55 @@ def test_cache_write_many_tokens(pa):
     pa.kv_cache_write(dev(k), dev(v), dev(slots), gk, gv)
     torch.cuda.synchronize()
     assert host(gk).tobytes() == ek.tobytes() and host(gv).tobytes() == ev.tobytes()
+
+
+def contexts_with_chunks(rng, b, target, ct=32, most=5):
+    # b contexts (some empty) whose ceil(ctx / ct) sum to exactly `target`
+    chunks = rng.integers(0, most + 1, b)
+    while chunks.sum() != target:
+        i = int(rng.integers(0, b))
+        if chunks.sum() < target and chunks[i] < most:
+            chunks[i] += 1
+        elif chunks.sum() > target and chunks[i] > 0:
+            chunks[i] -= 1
+    low = np.maximum((chunks - 1) * ct + 1, 0)
+    ctx = np.where(chunks > 0, rng.integers(low, chunks * ct + 1), 0)
+    assert int(((ctx + ct - 1) // ct).sum()) == target
+    return ctx.astype(np.int32)
+
+
+@pytest.mark.parametrize("b", [64, 65])
+@pytest.mark.parametrize("target", [159, 160, 161])
+@pytest.mark.parametrize("part", [0, 64])
+def test_split_regimes_around_the_boundary_charge(pa, b, target, part):
+    # 32 query / 8 KV heads, D 64: 32-token units, 8 units per chunk of a
+    # sequence.  160 chunks (1280 units) is where the split starts charging
+    # a segment change; 64 sequences keep the prefix sums in registers, 65
+    # use the workgroup's LDS.  Empty contexts are mixed in.
+    rng = np.random.default_rng(1000 + 10 * b + target + part)
+    ctx = contexts_with_chunks(rng, b, target)
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 0, 32, 8, 64, ctx_list=ctx)
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    got = gpu_decode(pa, q, kc, vc, tables, ctx, 0.125, part=part)
+    assert_close(got, ref, np.float32, f"B={b} chunks={target} part={part}")
+    assert (di.as_float64(got[ctx == 0]) == 0).all()
+
+
+@pytest.mark.parametrize("b", [64, 65])
+def test_split_regimes_bf16_fused_step(pa, b):
+    # the same boundary for bf16 storage through the fused append + decode
+    rng = np.random.default_rng(2000 + b)
+    ctx = contexts_with_chunks(rng, b, 161)
+    ctx = np.maximum(ctx, 1).astype(np.int32)
+    q, kc, vc, tables, ctx = random_case(rng, di.BF16, 0, 32, 8, 64, ctx_list=ctx)
+    k_new = di.cast(rng.standard_normal((b, 8, 64)), di.BF16)
+    v_new = di.cast(rng.standard_normal((b, 8, 64)), di.BF16)
+    slots = derived_slots(tables, ctx)
+    kw, vw = oracle.kv_cache_write(k_new, v_new, slots, kc, vc)
+    ref = oracle.paged_attn_decode(q, kw, vw, tables, ctx, 0.125)
+    kcd, vcd = dev(kc), dev(vc)
+    out = pa.paged_attn_decode_step(dev(q), dev(k_new), dev(v_new), kcd, vcd, dev(tables),
+                                    dev(ctx), 0.125, max_context_len=int(ctx.max()))
+    torch.cuda.synchronize()
+    assert_close(host(out), ref, di.BF16, f"fused B={b}")
+    assert host(kcd).tobytes() == kw.tobytes() and host(vcd).tobytes() == vw.tobytes()
