@@ -106,11 +106,11 @@ typedef struct photon_decode_desc {
                                    the wavefronts this implies, but over no
                                    more than one per five quanta of it (a
                                    slice is never much shorter than five)
-                                   unless that leaves fewer than 256; when
-                                   slices hold five quanta or more, a
-                                   wavefront whose slice moves on to another
-                                   (sequence, KV head) is charged two quanta
-                                   for the change                             */
+                                   unless that leaves fewer than 256; in a
+                                   batch of 768 quanta or more, a wavefront
+                                   whose slice moves on to another (sequence,
+                                   KV head) is charged two quanta for the
+                                   change                                     */
     photon_kv_desc kv;
     int32_t flags;              /* PHOTON_DECODE_* bits, 0 = none; other bits
                                    are PHOTON_ERR_INVALID_ARG                    */

@@ -12,8 +12,8 @@
 // so every K/V byte is fetched from HBM once.  A segment is cut into chunks
 // of CT = 16 U tokens; the chunks of all segments, sequence-major then
 // KV-head-major, form one list of U_tot units.  In the list the waves
-// split, each non-empty segment is preceded by C empty entries (C = 2 once
-// slices hold five units or more, else 0); of the wavefronts launched,
+// split, each non-empty segment is preceded by C empty entries (C = 2 for
+// batches of 768 units or more, else 0); of the wavefronts launched,
 // NW = min(launched, max(ceil(L / 5), min(U_tot, 256))) take part, for L
 // list entries, and wave s takes entries [s L / NW, (s+1) L / NW): every wave gets
 // the same amount of work however ragged the contexts are, a slice that
@@ -94,12 +94,15 @@ constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kMinUnitsPerWave = 5;
 constexpr int kMinWaves = 256;
 // Work a wavefront is charged for starting on a segment, in units: a piece
-// change costs a record, an arrival and a fresh first round trip, so when
-// slices hold kMinUnitsPerWave units or more, each non-empty segment is
-// counted as this many units longer (empty units at its start).  A slice
-// that spans a segment change then holds that many fewer chunks.  Two was
-// measured best among one to three (ragged batch-64: 29.6 -> 28.2 us).
+// change costs a record, an arrival and a fresh first round trip, so in a
+// batch of at least kChargeFromUnits units each non-empty segment is counted
+// as this many units longer (empty units at its start).  A slice that spans
+// a segment change then holds that many fewer chunks.  Two was measured
+// best among one to three (ragged batch-64: 29.6 -> 28.2 us).  From
+// 3 * kMinWaves units on, every slice holds at least three list entries, so
+// at least one unit of work (batch 4: 14.8 -> 13.6 us at fp32).
 constexpr int kBoundaryUnits = 2;
+constexpr int kChargeFromUnits = 3 * kMinWaves;
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -768,16 +771,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         }
     }
     // Slices split the list in which every non-empty segment starts with C
-    // empty units (none for small calls, whose slices hold one or two
-    // units).  At most one wavefront per kMinUnitsPerWave entries of that
+    // empty units (none for small calls, whose slices would hold one or two
+    // entries).  At most one wavefront per kMinUnitsPerWave entries of that
     // list, but no fewer than kMinWaves (or one per unit): a wave's fixed
     // costs (prefix, first table window and round trip, record, arrival,
     // merge) are paid once per slice, and fewer, longer slices also mean
     // fewer records and arrivals per segment, until too few waves are left
-    // to hide memory latency.  Slices hold at least four list entries when
+    // to hide memory latency.  Slices hold at least three list entries when
     // C > 0, so every slice holds work, and every slice between two others
     // holds a record of any segment spanning them.
-    const int C = total >= kMinUnitsPerWave * kMinWaves ? kBoundaryUnits : 0;
+    const int C = total >= kChargeFromUnits ? kBoundaryUnits : 0;
     const int total_v = total + C * hkv * ne_of(B - 1);
     const int nw = min(a.num_waves, max((total_v + kMinUnitsPerWave - 1) / kMinUnitsPerWave,
                                         min(total, kMinWaves)));
