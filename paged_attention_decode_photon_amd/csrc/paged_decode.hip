@@ -584,13 +584,15 @@ struct WaveDecoder {
 
     // Merge the records of every piece of segment (sb, sg), units [su0, su1),
     // in slice order, and write the normalised output.  Each lane folds four
-    // consecutive outputs of one head; kBatch records are loaded at a time.
+    // consecutive outputs of one head; kBatch records are loaded at a time
+    // (sixteen: one round trip for the 16 one-unit pieces of a batch-1
+    // segment of 512 tokens; the registers of the chunk loop are free here).
     // The segment's units are [su0, su1) of the slice list, after its empty
     // units, which start at sv0: a slice that starts at or after sv0 has this
     // segment as its first piece.
     __device__ void merge_segment(int sb, int sg, int sv0, int su0, int su1, int total, int nw) const
     {
-        constexpr int kBatch = 8;
+        constexpr int kBatch = 16;
         const int s_first = slice_of(su0, total, nw);
         const int s_last = slice_of(su1 - 1, total, nw);
         const int first_role = slice_start(s_first, total, nw) >= sv0 ? 0 : 1;
