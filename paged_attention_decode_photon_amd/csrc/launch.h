@@ -51,6 +51,14 @@ constexpr int decode_record_floats(int head_dim, int group)
     return (2 * group + group * head_dim + 3) & ~3;
 }
 
+// Multi-query calls whose longest query run spans at least this many
+// 16-row tiles use the wide kernel (four tiles per workgroup sharing each
+// K/V block through LDS); shorter ones the per-tile kernel.
+#ifndef PHOTON_MQ_WIDE_TILES
+#define PHOTON_MQ_WIDE_TILES 4
+#endif
+constexpr int kWideTiles = PHOTON_MQ_WIDE_TILES;
+
 // Sequences per call: the decode kernel keeps per-sequence prefix sums in LDS.
 constexpr int kMaxDecodeSeqs = 2048;
 

@@ -68,12 +68,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(float *rec, int float
 }
 constexpr int kRawWord3 = 0x00020000;
 constexpr int kTile = 16;  // query rows per tile, tokens per KV block
-// Calls whose longest query run spans at least this many tiles use the wide
-// kernel (four tiles per workgroup sharing each K/V block through LDS).
-#ifndef PHOTON_MQ_WIDE_TILES
-#define PHOTON_MQ_WIDE_TILES 4
-#endif
-constexpr int kWideTiles = PHOTON_MQ_WIDE_TILES;
 
 __device__ __forceinline__ void wave_sync()
 {

@@ -192,8 +192,12 @@ struct MqPlan {
 // workgroups (four per compute unit of an MI355X).
 constexpr int64_t kMqTargetGroups = 1024;
 // ... but no split shorter than 32 blocks: each wave then runs at least four
-// blocks, two at a time (measured best for 4-token verification at batch 16).
+// blocks, two at a time (measured best for 16-bit 4-token verification at
+// batch 16) ...
 constexpr int64_t kMqMinSplitBlocks = 32;
+// ... or 16 blocks for fp32 storage in the per-tile kernel, whose blocks take
+// twice the bytes (4-token verification at batch 16: 26.5 -> 25.5 us).
+constexpr int64_t kMqMinSplitBlocksF32 = 16;
 // ... and none longer than 64 blocks (1024 tokens): a long prompt chunk at a
 // long context is then spread over several workgroups.
 constexpr int64_t kMqMaxSplitBlocks = 64;
@@ -246,7 +250,10 @@ photon_status plan_multi_query(const photon_multi_query_desc *d, MqPlan *plan)
         const int64_t want = tiles > 0 ? (kMqTargetGroups + tiles - 1) / tiles : 1;
         sb = want > 1 ? (max_nblk + want - 1) / want : max_nblk;
         sb = (sb + 7) / 8 * 8;  // whole steps: four waves, two blocks each
-        sb = sb < kMqMinSplitBlocks ? kMqMinSplitBlocks : sb;
+        const int64_t min_sb = elem_bytes_of(d->kv.dtype) == 4 && p.max_tiles < photon::kWideTiles
+                                   ? kMqMinSplitBlocksF32
+                                   : kMqMinSplitBlocks;
+        sb = sb < min_sb ? min_sb : sb;
         sb = sb > kMqMaxSplitBlocks ? kMqMaxSplitBlocks : sb;
     }
     const int64_t splits = max_nblk > sb ? (max_nblk + sb - 1) / sb : 1;

@@ -266,10 +266,19 @@ def test_multi_query_split_and_workspace_formula():
     n = ctypes.c_size_t(0)
     assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
     # automatic: 1024 / 32 = 32 splits wanted -> 4 blocks each, raised to the
-    # 32-block minimum -> ceil(125/32) = 4 splits
+    # fp32 per-tile minimum of 16 blocks -> ceil(125/16) = 8 splits
     counters = (32 * 4 + 255) // 256 * 256
     rec = 16 * (64 + 2) * 4
+    assert n.value == counters + 32 * 8 * rec
+    # 16-bit storage: the 32-block minimum -> ceil(125/32) = 4 splits
+    d16 = mqd(mb=128, maxctx=2000, dtype=pa.F16)
+    assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(d16), ctypes.byref(n)) == 0
     assert n.value == counters + 32 * 4 * rec
+    # fp32 with a query run of four tiles (the wide kernel): 32-block minimum
+    dw = mqd(b=1, t=16, mq=16, mb=128, maxctx=2000)
+    assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(dw), ctypes.byref(n)) == 0
+    assert n.value == (8 * 4 + 255) // 256 * 256 + 8 * 4 * 4 * rec
+    d = mqd(mb=128, maxctx=2000)
     # explicit 512-token splits: 4 splits of 32 blocks
     d = mqd(mb=128, maxctx=2000, split=512)
     assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
