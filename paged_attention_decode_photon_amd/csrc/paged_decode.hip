@@ -189,12 +189,13 @@ struct KernelArgs {
     float qscale;
 };
 
-// First unit of slice s (slices split [0, total) as evenly as integers allow).
+// First list entry of slice s (slices split [0, total) as evenly as integers
+// allow).
 __device__ __forceinline__ int slice_start(int s, int total, int nw)
 {
     return (int)(((long long)s * total) / nw);
 }
-// Slice that holds unit u: the largest s with slice_start(s) <= u.
+// Slice that holds list entry u: the largest s with slice_start(s) <= u.
 __device__ __forceinline__ int slice_of(int u, int total, int nw)
 {
     return (int)((((long long)u + 1) * nw - 1) / total);
