@@ -5,18 +5,23 @@ kernels of ``libphoton_decode.so`` (built from ``csrc/`` by ``build.py``).
 Functions take torch tensors on a ROCm device, pass their data pointers and
 the current HIP stream through the C ABI declared in
 ``include/photon_decode.h``, and raise :class:`PhotonError` on a non-OK
-status.  There is no fallback: if the library is missing, importing this
-package raises.
+status.  There is no fallback: the library is loaded on the first call
+that needs it (or the first access to ``lib``), and that call raises
+ImportError if the library is missing.  Importing the package itself loads
+nothing, so ``python -m paged_attention_decode_photon_amd.build`` works on a
+fresh checkout.
 
 The library must run inside the same HIP runtime as PyTorch (it uses torch's
 streams and allocations), so torch is imported before the library is loaded:
 the dynamic loader then binds the library's ``libamdhip64.so.7`` dependency
-to the copy torch already mapped.  Import fails if two runtimes end up mapped.
+to the copy torch already mapped.  Loading fails if two runtimes end up
+mapped.
 """
 from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libphoton_decode.so")
@@ -124,11 +129,30 @@ def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-lib = _load_library()
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def get_lib() -> ctypes.CDLL:
+    """The loaded ``libphoton_decode.so`` (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        with _lib_lock:
+            if _lib is None:
+                _lib = _load_library()
+    return _lib
+
+
+def __getattr__(name: str):
+    # ``lib`` is loaded lazily (PEP 562 module attribute)
+    if name == "lib":
+        return get_lib()
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
 
 
 def check(status: int) -> None:
     if status != OK:
+        lib = get_lib()
         raise PhotonError(status, lib.photon_status_str(status).decode(),
                           lib.photon_last_error_detail().decode())
 
@@ -154,6 +178,30 @@ def _contig(name: str, t) -> None:
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", f"{name} is not contiguous")
 
 
+def _args_ok(device, **tensors) -> None:
+    """Every tensor is contiguous and lives on ``device``, a GPU.
+
+    The kernels dereference every pointer they get on the GPU, so a host
+    tensor (or one on another GPU) is refused here rather than handed over.
+    """
+    if device.type != "cuda":
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          f"tensors must be on a ROCm GPU, not {device}")
+    for name, t in tensors.items():
+        _contig(name, t)
+        if t.device != device:
+            raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                              f"{name} is on {t.device}, the pools on {device}")
+
+
+def _int32(**tensors) -> None:
+    import torch
+    for name, t in tensors.items():
+        if t.dtype != torch.int32:
+            raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                              f"{name} must be int32, not {t.dtype}")
+
+
 def kv_desc(k_cache) -> KvDesc:
     nb, hkv, bs, d = k_cache.shape
     return KvDesc(nb, hkv, bs, d, _dtype_code(k_cache))
@@ -168,9 +216,9 @@ def decode_desc(q, k_cache, block_tables, max_context_len: int,
 
 def kv_cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
     """Write k[i], v[i] ([T, Hkv, D]) into pool slot ``slot_mapping[i]`` (in place)."""
-    for name, t in (("k", k), ("v", v), ("slot_mapping", slot_mapping), ("k_cache", k_cache),
-                    ("v_cache", v_cache)):
-        _contig(name, t)
+    _int32(slot_mapping=slot_mapping)
+    _args_ok(k_cache.device, k=k, v=v, slot_mapping=slot_mapping, k_cache=k_cache,
+             v_cache=v_cache)
     if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "k, v and pools differ in dtype")
     _, hkv, _, d = k_cache.shape
@@ -178,7 +226,7 @@ def kv_cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
             or v_cache.shape != k_cache.shape:
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
     desc = kv_desc(k_cache)
-    check(lib.photon_kv_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+    check(get_lib().photon_kv_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
                                     slot_mapping.shape[0], k_cache.data_ptr(), v_cache.data_ptr(),
                                     ctypes.byref(desc), _stream_ptr(k_cache)))
 
@@ -192,14 +240,11 @@ def rope_kv_cache_write(q, k, v, positions, slot_mapping, k_cache, v_cache, base
     tensor unless given; passing q itself rotates q in place).
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("positions", positions),
-                    ("slot_mapping", slot_mapping), ("k_cache", k_cache), ("v_cache", v_cache)):
-        _contig(name, t)
+    _int32(positions=positions, slot_mapping=slot_mapping)
+    _args_ok(k_cache.device, q=q, k=k, v=v, positions=positions, slot_mapping=slot_mapping,
+             k_cache=k_cache, v_cache=v_cache)
     if any(t.dtype != k_cache.dtype for t in (q, k, v, v_cache)):
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q, k, v and pools differ in dtype")
-    if positions.dtype != torch.int32 or slot_mapping.dtype != torch.int32:
-        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
-                          "positions and slot_mapping must be int32")
     t_, hq, d = q.shape
     _, hkv, _, d2 = k_cache.shape
     if d != d2 or tuple(k.shape) != (t_, hkv, d) or v.shape != k.shape \
@@ -209,12 +254,12 @@ def rope_kv_cache_write(q, k, v, positions, slot_mapping, k_cache, v_cache, base
     if q_out is None:
         q_out = torch.empty_like(q)
     else:
-        _contig("q_out", q_out)
+        _args_ok(k_cache.device, q_out=q_out)
         if q_out.shape != q.shape or q_out.dtype != q.dtype:
             raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q_out shape or dtype")
     desc = kv_desc(k_cache)
     rope = RopeDesc(float(base), int(bool(adjacent_pairs)), 0)
-    check(lib.photon_rope_kv_cache_write(q.data_ptr(), q_out.data_ptr(), k.data_ptr(), v.data_ptr(),
+    check(get_lib().photon_rope_kv_cache_write(q.data_ptr(), q_out.data_ptr(), k.data_ptr(), v.data_ptr(),
                                          positions.data_ptr(), slot_mapping.data_ptr(), t_, hq,
                                          k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(desc),
                                          ctypes.byref(rope), _stream_ptr(k_cache)))
@@ -222,24 +267,24 @@ def rope_kv_cache_write(q, k, v, positions, slot_mapping, k_cache, v_cache, base
 
 
 def partition_quantum(desc: DecodeDesc) -> int:
-    n = lib.photon_paged_attn_partition_quantum(ctypes.byref(desc))
+    n = get_lib().photon_paged_attn_partition_quantum(ctypes.byref(desc))
     if n == 0:
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
-                          lib.photon_last_error_detail().decode())
+                          get_lib().photon_last_error_detail().decode())
     return n
 
 
 def partition_tokens(desc: DecodeDesc) -> int:
-    n = lib.photon_paged_attn_partition_tokens(ctypes.byref(desc))
+    n = get_lib().photon_paged_attn_partition_tokens(ctypes.byref(desc))
     if n == 0:
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
-                          lib.photon_last_error_detail().decode())
+                          get_lib().photon_last_error_detail().decode())
     return n
 
 
 def workspace_bytes(desc: DecodeDesc) -> int:
     n = ctypes.c_size_t(0)
-    check(lib.photon_paged_attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    check(get_lib().photon_paged_attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
     return n.value
 
 
@@ -263,12 +308,9 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
     float32 with 16-bit storage selects the fp32-output kernels.
     """
     import torch
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
-                    ("block_tables", block_tables), ("context_lens", context_lens)):
-        _contig(name, t)
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
-                          "block_tables and context_lens must be int32")
+    _int32(block_tables=block_tables, context_lens=context_lens)
+    _args_ok(k_cache.device, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+             context_lens=context_lens)
     if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q and pools differ")
     if q.shape[2] != k_cache.shape[3] or block_tables.shape[0] != q.shape[0] \
@@ -289,14 +331,16 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     else:
-        _contig("out", out)
+        _args_ok(k_cache.device, out=out)
         if out.shape != q.shape:
             raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape")
     if ws_need and workspace is None:
         workspace = new_workspace(ws_need, q.device)
+    if workspace is not None:
+        _args_ok(k_cache.device, workspace=workspace)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib.photon_paged_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+    check(get_lib().photon_paged_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                        block_tables.data_ptr(), context_lens.data_ptr(),
                                        float(scale), ctypes.byref(desc), out.data_ptr(), ws_ptr,
                                        ws_len, _stream_ptr(q)))
@@ -312,7 +356,7 @@ def multi_query_desc(q, k_cache, block_tables, num_seqs: int, max_query_len: int
 
 def multi_query_workspace_bytes(desc: MultiQueryDesc) -> int:
     n = ctypes.c_size_t(0)
-    check(lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    check(get_lib().photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
     return n.value
 
 
@@ -331,12 +375,9 @@ def paged_attn_multi_query(q, k_cache, v_cache, block_tables, context_lens, quer
     ``workspace`` is allocated through torch when needed and not given.
     """
     import torch
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
-                    ("block_tables", block_tables), ("context_lens", context_lens),
-                    ("query_start", query_start)):
-        _contig(name, t)
-    if any(t.dtype != torch.int32 for t in (block_tables, context_lens, query_start)):
-        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "index tensors must be int32")
+    _int32(block_tables=block_tables, context_lens=context_lens, query_start=query_start)
+    _args_ok(k_cache.device, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+             context_lens=context_lens, query_start=query_start)
     if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q and pools differ")
     b = context_lens.shape[0]
@@ -358,7 +399,7 @@ def paged_attn_multi_query(q, k_cache, v_cache, block_tables, context_lens, quer
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     else:
-        _contig("out", out)
+        _args_ok(k_cache.device, out=out)
         if out.shape != q.shape:
             raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape")
     desc = multi_query_desc(q, k_cache, block_tables, b, max_query_len, max_context_len,
@@ -366,9 +407,11 @@ def paged_attn_multi_query(q, k_cache, v_cache, block_tables, context_lens, quer
     ws_need = multi_query_workspace_bytes(desc)
     if ws_need and workspace is None:
         workspace = new_workspace(ws_need, q.device)
+    if workspace is not None:
+        _args_ok(k_cache.device, workspace=workspace)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib.photon_paged_attn_multi_query(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+    check(get_lib().photon_paged_attn_multi_query(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                             block_tables.data_ptr(), context_lens.data_ptr(),
                                             query_start.data_ptr(), float(scale), ctypes.byref(desc),
                                             out.data_ptr(), ws_ptr, ws_len, _stream_ptr(q)))
@@ -381,13 +424,9 @@ def paged_attn_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, cont
     """One fused decode step: store k_new[b], v_new[b] ([B, Hkv, D]) at position
     context_lens[b] - 1 of each sequence, then attend as :func:`paged_attn_decode`."""
     import torch
-    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
-                    ("v_cache", v_cache), ("block_tables", block_tables),
-                    ("context_lens", context_lens)):
-        _contig(name, t)
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
-                          "block_tables and context_lens must be int32")
+    _int32(block_tables=block_tables, context_lens=context_lens)
+    _args_ok(k_cache.device, q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+             block_tables=block_tables, context_lens=context_lens)
     if any(t.dtype != k_cache.dtype for t in (q, k_new, v_new, v_cache)) or v_cache.shape != k_cache.shape:
         raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q, new rows and pools differ")
     b, _, d = q.shape
@@ -402,14 +441,16 @@ def paged_attn_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, cont
     if out is None:
         out = torch.empty_like(q)
     else:
-        _contig("out", out)
+        _args_ok(k_cache.device, out=out)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "out shape or dtype")
     if ws_need and workspace is None:
         workspace = new_workspace(ws_need, q.device)
+    if workspace is not None:
+        _args_ok(k_cache.device, workspace=workspace)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib.photon_paged_attn_decode_step(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+    check(get_lib().photon_paged_attn_decode_step(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                                             k_cache.data_ptr(), v_cache.data_ptr(),
                                             block_tables.data_ptr(), context_lens.data_ptr(),
                                             float(scale), ctypes.byref(desc), out.data_ptr(),

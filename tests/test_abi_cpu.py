@@ -340,3 +340,44 @@ def test_decode_step_rejects_missing_new_rows():
     assert call(FAKE, FAKE + 4) == pa.ERR_INVALID_ARG
     assert pa.lib.photon_paged_attn_decode_step(None, None, None, None, None, None, None, 0.125,
                                                 ctypes.byref(dd(b=0)), None, None, 0, None) == pa.OK
+
+
+def _binding_calls(torch, idx_dtype):
+    """One call of each binding on host tensors, with index tensors of idx_dtype."""
+    f32 = torch.float32
+    kc = torch.zeros((4, 2, 16, 64), dtype=f32)
+    vc = torch.zeros_like(kc)
+    q = torch.zeros((1, 4, 64), dtype=f32)
+    k = torch.zeros((1, 2, 64), dtype=f32)
+    idx1 = torch.zeros(1, dtype=idx_dtype)
+    tables = torch.zeros((1, 4), dtype=idx_dtype)
+    qs = torch.tensor([0, 1], dtype=idx_dtype)
+    return {
+        "kv_cache_write": lambda: pa.kv_cache_write(k, k, idx1, kc, vc),
+        "rope_kv_cache_write": lambda: pa.rope_kv_cache_write(q, k, k, idx1, idx1, kc, vc, 1e4),
+        "paged_attn_decode": lambda: pa.paged_attn_decode(q, kc, vc, tables, idx1, 0.125,
+                                                          max_context_len=1),
+        "paged_attn_decode_step": lambda: pa.paged_attn_decode_step(q, k, k, kc, vc, tables, idx1,
+                                                                    0.125, max_context_len=1),
+        "paged_attn_multi_query": lambda: pa.paged_attn_multi_query(
+            q, kc, vc, tables, idx1, qs, 0.125, max_query_len=1, max_context_len=1),
+    }
+
+
+@pytest.mark.parametrize("entry", ["kv_cache_write", "rope_kv_cache_write", "paged_attn_decode",
+                                   "paged_attn_decode_step", "paged_attn_multi_query"])
+def test_binding_refuses_int64_indices(entry):
+    # torch's default integer type is int64; the kernels read int32, so an
+    # int64 slot mapping or table would be misread.  The binding refuses it.
+    torch = pytest.importorskip("torch")
+    with pytest.raises(pa.PhotonError, match="int32"):
+        _binding_calls(torch, torch.int64)[entry]()
+
+
+@pytest.mark.parametrize("entry", ["kv_cache_write", "rope_kv_cache_write", "paged_attn_decode",
+                                   "paged_attn_decode_step", "paged_attn_multi_query"])
+def test_binding_refuses_host_tensors(entry):
+    # a host pointer handed to a kernel would be dereferenced on the GPU
+    torch = pytest.importorskip("torch")
+    with pytest.raises(pa.PhotonError, match="GPU"):
+        _binding_calls(torch, torch.int32)[entry]()
