@@ -31,7 +31,19 @@
  *   - Device-resident indices (slot_mapping, block_tables, context_lens) are
  *     NOT range-checked by the kernels: out-of-range values are a caller
  *     error and may fault the GPU.
- *   - Functions hold no global state and may be called from several threads.
+ *   - Functions may be called from several threads.  The library's only
+ *     state is a process-wide call counter (see "Workspaces" below).
+ *   - Workspaces.  Calls that split work over several wavefronts take a
+ *     caller-provided workspace for partial results and per-segment arrival
+ *     counters.  Its contents before a call do not matter: it need not be
+ *     cleared, ever.  Each counter is a 64-bit word whose upper half is
+ *     tagged with the number the library gives every call, and a call
+ *     replaces any value tagged otherwise before counting on it (so neither
+ *     uninitialised memory nor a call that never finished can corrupt a
+ *     later call; a stale value is missed only if its tag happens to equal
+ *     the new call's number, one chance in 2^32).  A call that finishes
+ *     leaves every counter at 0.  Calls that may run at the same time (on
+ *     different streams) need workspaces of their own.
  */
 #ifndef PHOTON_DECODE_H
 #define PHOTON_DECODE_H
@@ -43,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PHOTON_ABI_VERSION 6
+#define PHOTON_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define PHOTON_API __attribute__((visibility("default")))
@@ -158,10 +170,10 @@ typedef struct photon_multi_query_desc {
 
 /*
  * Workspace bytes photon_paged_attn_multi_query needs for desc: 0 when no
- * tile's KV range is split, else one int32 arrival counter per tile of 16
- * query rows, then one fp32 record of 16 * (head_dim + 2) floats per tile
- * and split.  Zero-filled once before first use; every completed call leaves
- * the counters at zero.  Concurrent calls need workspaces of their own.
+ * tile's KV range is split, else one 64-bit arrival counter per tile of 16
+ * query rows (padded to 256 bytes), then one fp32 record of
+ * 16 * (head_dim + 2) floats per tile and split.  Its contents before a call
+ * do not matter (see "Workspaces" above).
  */
 PHOTON_API photon_status photon_paged_attn_multi_query_workspace_bytes(
     const photon_multi_query_desc *desc, size_t *bytes);
@@ -270,19 +282,17 @@ PHOTON_API int32_t photon_paged_attn_partition_quantum(const photon_decode_desc 
 PHOTON_API int32_t photon_paged_attn_partition_tokens(const photon_decode_desc *desc);
 
 /*
- * Workspace bytes photon_paged_attn_decode needs for desc (0 only when
- * num_seqs is 0).  Layout: one int32 arrival counter per (sequence, KV head),
- * then two fp32 partial records per wavefront (running maximum and
- * exponential sum of each query head of a group, then their unnormalised
- * output rows).
- *
- * The workspace must be zero-filled once before its first use (for example
- * allocated with torch.zeros or cleared with hipMemset).  Every call that
- * completes leaves the counters at zero again, so the same workspace serves
- * later calls of any shape without clearing.  Calls that may run at the same
- * time (other streams) need workspaces of their own.
+ * Workspace bytes photon_paged_attn_decode needs for desc: 0 when num_seqs
+ * is 0 or max_context_len is at most one partition quantum (no context is
+ * then ever split), else one 64-bit arrival counter per (sequence, KV head),
+ * padded to 256 bytes, then two fp32 partial records per wavefront (the
+ * unnormalised output rows of the query heads of a group, then their running
+ * maxima and exponential sums).  Its contents before a call do not matter
+ * (see "Workspaces" above): the same workspace serves later calls of any
+ * shape it is large enough for, without clearing.
  */
-PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_desc *desc, size_t *bytes);
+PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_desc *desc,
+                                                           size_t *bytes);
 
 /*
  * Batched paged-attention decode with grouped-query heads (README "GPU-
@@ -304,12 +314,13 @@ PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_d
  *   q             [num_seqs, num_q_heads, head_dim]        kv.dtype, 16-byte aligned
  *   k_cache, v_cache  pools (read only), 16-byte aligned
  *   block_tables  [num_seqs, max_blocks_per_seq] int32, entries < kv.num_blocks
- *   context_lens  [num_seqs] int32, 0 <= ctx <= max_context_len
+ *   context_lens  [num_seqs] int32, 0 <= ctx <= max_context_len (a longer
+ *                 context is a caller error: with no workspace it may fault)
  *   out           [num_seqs, num_q_heads, head_dim]        kv.dtype (fp32 with
  *                 PHOTON_DECODE_OUT_F32), 16-byte aligned
  *   workspace     device scratch of workspace_bytes >= the size the workspace
- *                 query returns, 16-byte aligned, zero-filled before its first
- *                 use
+ *                 query returns, 16-byte aligned, any contents; may be NULL
+ *                 when that size is 0
  */
 PHOTON_API photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                                        const int32_t *block_tables, const int32_t *context_lens,

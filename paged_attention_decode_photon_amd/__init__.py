@@ -289,9 +289,10 @@ def workspace_bytes(desc: DecodeDesc) -> int:
 
 
 def new_workspace(nbytes: int, device):
-    """Zero-filled workspace tensor (the counters in it must start at zero)."""
+    """Workspace tensor of at least ``nbytes`` (its contents do not matter:
+    the arrival counters in it are tagged with each call's number)."""
     import torch
-    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,

@@ -71,7 +71,7 @@ struct DecodeArgs {
     const int32_t *block_tables;
     const int32_t *context_lens;
     void *out;
-    int *ws_count;  // [B][Hkv] units merged so far per segment; zero between calls
+    uint64_t *ws_count;  // [B][Hkv] epoch-tagged arrival counters (arrival.h)
     float *ws_rec;  // [num_waves][2] partial records of decode_record_floats each
     int num_seqs;
     int num_kv_heads;
@@ -83,6 +83,7 @@ struct DecodeArgs {
     int max_blocks;
     int num_waves;  // wavefronts launched; a multiple of kDecodeWaves
     float qscale;   // scale * log2(e)
+    uint32_t epoch; // this call's number (never 0): tags the arrival counters
 };
 
 // One decode launch on stream (partitions merge inside the same kernel).
@@ -104,11 +105,12 @@ struct MultiQueryArgs {
     int max_tiles;  // ceil(max_query_len * group / 16): grid x
     int split_blocks;  // KV blocks per split of a tile's causal range
     int num_splits;    // grid z: splits of the longest range
-    int *ws_count;     // [B * Hkv * max_tiles] arrival counters, zero between calls
+    uint64_t *ws_count;  // [B * Hkv * max_tiles] epoch-tagged arrival counters (arrival.h)
     float *ws_rec;     // [B * Hkv * max_tiles * num_splits] records of 16 * (D + 2) floats
     int dtype;
     int out_f32;
     float qscale;   // scale * log2(e)
+    uint32_t epoch; // this call's number (never 0): tags the arrival counters
 };
 
 // Multi-query paged attention with a causal tail, one launch.

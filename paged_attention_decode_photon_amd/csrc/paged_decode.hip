@@ -29,10 +29,11 @@
 // A wave's slice covers pieces of one or more segments.  A piece that holds
 // a whole segment writes its normalised output directly.  Otherwise the
 // piece's (max, sum, unnormalised rows) go to a workspace record and the
-// wave adds the piece's unit count to the segment's arrival counter; the
-// wave that completes the count merges all pieces of the segment in slice
-// order (deterministic whichever wave that is) and resets the counter to
-// zero.  Waves of one segment may run on different XCDs, whose L2 caches are
+// wave adds the piece's unit count to the segment's arrival counter (tagged
+// with the call's epoch, so whatever the workspace held before the call is
+// never counted; arrival.h); the wave that completes the count merges all
+// pieces of the segment in slice order (deterministic whichever wave that
+// is) and resets the counter to zero.  Waves of one segment may run on different XCDs, whose L2 caches are
 // not coherent with each other; rather than agent-scope fences (an L2
 // write-back or invalidate, far too slow here) only the partial results
 // travel coherently, as device-scope (sc1) stores and loads, and a wave's
@@ -76,6 +77,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "arrival.h"
 #include "elem.h"
 #include "lane_ops.h"
 #include "launch.h"
@@ -180,13 +182,14 @@ struct KernelArgs {
     const int32_t *block_tables;
     const int32_t *context_lens;
     void *out;
-    int *ws_count;
+    uint64_t *ws_count;  // epoch-tagged arrival counters (arrival.h)
     float *ws_rec;
     int num_seqs;
     int num_kv_heads;
     int max_blocks;
     int num_waves;
     float qscale;
+    uint32_t epoch;  // this call's number, never 0
 };
 
 // First list entry of slice s (slices split [0, total) as evenly as integers
@@ -821,6 +824,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     // then, should this wave have completed the segment).
     bool pend = false, pend_count_now = false;
     int pend_b = 0, pend_g = 0, pend_seg = 0, pend_nch = 0, pend_units = 0, pend_old = 0;
+    uint64_t pend_seen = 0;  // lane 0: what the pending piece's claim found
     while (true) {
         const int seq_end = end_of(b) + C * hkv * ne_of(b);
         const int ctx = ctx_of(b);
@@ -846,8 +850,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
             wait_vector_memory();
             int old = 0;
             if (lane == 0)
-                old = __hip_atomic_fetch_add(&a.ws_count[(size_t)pend_b * hkv + pend_g], pend_units,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                old = (int)arrive_counter(&a.ws_count[(size_t)pend_b * hkv + pend_g], a.epoch,
+                                          pend_seen, pend_units);
             pend_old = old;
             pend_count_now = false;
         }
@@ -858,8 +862,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         } else {
             const int role = first_piece ? 0 : 1;
             w.store_record(a.ws_rec + ((size_t)s * 2 + role) * S::REC);
+            // Claim the segment's counter for this call; the wait for the
+            // record stores below also covers the swap.
+            uint64_t seen = 0;
+            if (lane == 0)
+                seen = claim_counter(&a.ws_count[(size_t)b * hkv + g], a.epoch);
             if (first_piece && r1 + C < v_end) {  // another piece follows in this slice
                 pend = pend_count_now = true;
+                pend_seen = seen;
                 pend_b = b;
                 pend_g = g;
                 pend_seg = seg_v0;
@@ -869,14 +879,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
                 wait_vector_memory();
                 int done = 0;
                 if (lane == 0)
-                    done = __hip_atomic_fetch_add(&a.ws_count[(size_t)b * hkv + g], ch1 - ch0,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    done = (int)arrive_counter(&a.ws_count[(size_t)b * hkv + g], a.epoch, seen,
+                                               ch1 - ch0);
                 done = __builtin_amdgcn_readfirstlane(done) + (ch1 - ch0);
                 if (done == nch) {
                     w.merge_segment(b, g, seg_v0, seg_v0 + C, seg_v0 + stride, total_v, nw);
                     if (lane == 0)
-                        __hip_atomic_store(&a.ws_count[(size_t)b * hkv + g], 0, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                        release_counter(&a.ws_count[(size_t)b * hkv + g]);
                 }
             }
         }
@@ -893,8 +902,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     if (pend && __builtin_amdgcn_readfirstlane(pend_old) + pend_units == pend_nch) {
         w.merge_segment(pend_b, pend_g, pend_seg, pend_seg + C, pend_seg + C + pend_nch, total_v, nw);
         if (lane == 0)
-            __hip_atomic_store(&a.ws_count[(size_t)pend_b * hkv + pend_g], 0, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            release_counter(&a.ws_count[(size_t)pend_b * hkv + pend_g]);
     }
 }
 
@@ -917,6 +925,7 @@ hipError_t launch_typed(const DecodeArgs &d, hipStream_t stream)
     a.max_blocks = d.max_blocks;
     a.num_waves = d.num_waves;
     a.qscale = d.qscale;
+    a.epoch = d.epoch;
     hipLaunchKernelGGL((paged_decode_kernel<T, O, D, G>), dim3(d.num_waves / kDecodeWaves),
                        dim3(kDecodeWaves * 64), 0, stream, a);
     return hipGetLastError();

@@ -46,6 +46,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "arrival.h"
 #include "elem.h"
 #include "lane_ops.h"
 #include "launch.h"
@@ -648,12 +649,16 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
                                                   rs, (kTile * D + kTile + orow) * 4, 0, kSc1);
         }
     }
+    // Claim the tile's counter for this call (arrival.h); the wait for the
+    // record stores also covers the swap.
+    uint64_t seen = 0;
+    if (threadIdx.x == 0)
+        seen = claim_counter(&a.ws_count[tile_id], a.epoch);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's record stores are done
     __syncthreads();                                   // ... and every thread's
     __shared__ int arrived;
     if (threadIdx.x == 0)
-        arrived = __hip_atomic_fetch_add(&a.ws_count[tile_id], 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) + 1;
+        arrived = (int)arrive_counter(&a.ws_count[tile_id], a.epoch, seen, 1) + 1;
     __syncthreads();
     if (arrived != nsplit)
         return;
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
             dst[e] = Elem<O>::from_float(acc[e] * inv);
     }
     if (threadIdx.x == 0)
-        __hip_atomic_store(&a.ws_count[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        release_counter(&a.ws_count[tile_id]);
 }
 
 // Wide variant for long query runs (chunked prefill): a workgroup takes four
@@ -943,11 +948,15 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
                                                   (kTile * D + kTile + lr) * 4, 0, kSc1);
         }
     }
+    // Claim the tile's counter for this call (arrival.h); the wait for the
+    // record stores also covers the swap.
+    uint64_t seen = 0;
+    if (lane == 0)
+        seen = claim_counter(&a.ws_count[tile_id], a.epoch);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the whole wave's record is stored
     int arrived = 0;
     if (lane == 0)
-        arrived = __hip_atomic_fetch_add(&a.ws_count[tile_id], 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) + 1;
+        arrived = (int)arrive_counter(&a.ws_count[tile_id], a.epoch, seen, 1) + 1;
     arrived = __builtin_amdgcn_readfirstlane(arrived);
     if (arrived != nsplit)
         return;
@@ -989,7 +998,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_wide_kernel(MultiQuery
                 dst[16 * t + i] = Elem<O>::from_float(acc[t][i] * inv);
     }
     if (lane == 0)
-        __hip_atomic_store(&a.ws_count[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        release_counter(&a.ws_count[tile_id]);
 }
 
 template <typename T, typename O, int D>

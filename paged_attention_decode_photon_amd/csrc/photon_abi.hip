@@ -6,6 +6,7 @@
 // the same status with or without a GPU, and nothing is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -38,6 +39,22 @@ photon_status ok()
 }
 
 const char *last_detail() { return g_detail; }
+
+namespace {
+std::atomic<uint32_t> g_calls{0};
+}  // namespace
+
+// Number of this call, never 0: it tags the workspace arrival counters, so
+// whatever a workspace held before a call is never counted by it.  This
+// process-wide counter is the library's only state.
+uint32_t next_epoch()
+{
+    uint32_t e;
+    do {
+        e = g_calls.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (e == 0);
+    return e;
+}
 
 }  // namespace photon
 
@@ -101,7 +118,7 @@ struct Plan {
     int quantum;      // tokens per chunk (unit of work)
     int part_tokens;  // chunk-aligned tokens per wave slice for the upper-bound batch
     int num_waves;
-    size_t count_bytes;  // arrival counters, one int per (sequence, KV head)
+    size_t count_bytes;  // arrival counters, one 64-bit word per (sequence, KV head)
     size_t ws_bytes;     // total
 };
 
@@ -170,9 +187,11 @@ photon_status plan_decode(const photon_decode_desc *d, Plan *plan)
     p.num_waves = (int)waves;
     const int64_t per_wave = upper > 0 ? (upper + waves - 1) / waves : 1;
     p.part_tokens = (int)(per_wave * p.quantum);
-    if (d->num_seqs > 0) {
+    // A segment of one unit is never split, so calls whose contexts all fit
+    // in one unit need no workspace.
+    if (d->num_seqs > 0 && chunks > 1) {
         const size_t rec = (size_t)photon::decode_record_floats(d->kv.head_dim, group) * sizeof(float);
-        p.count_bytes = align256((size_t)d->num_seqs * d->kv.num_kv_heads * sizeof(int));
+        p.count_bytes = align256((size_t)d->num_seqs * d->kv.num_kv_heads * sizeof(uint64_t));
         p.ws_bytes = p.count_bytes + (size_t)waves * 2 * rec;
     }
     *plan = p;
@@ -263,7 +282,7 @@ photon_status plan_multi_query(const photon_multi_query_desc *d, MqPlan *plan)
     p.num_splits = (int)splits;
     if (splits > 1 && tiles > 0) {
         const size_t rec = (size_t)16 * (d->kv.head_dim + 2) * sizeof(float);
-        p.count_bytes = align256((size_t)tiles * sizeof(int));
+        p.count_bytes = align256((size_t)tiles * sizeof(uint64_t));
         p.ws_bytes = p.count_bytes + (size_t)tiles * splits * rec;
     }
     *plan = p;
@@ -355,11 +374,12 @@ photon_status photon_paged_attn_multi_query(const void *q, const void *k_cache, 
     a.split_blocks = p.split_blocks;
     a.num_splits = p.num_splits;
     char *ws = static_cast<char *>(workspace);
-    a.ws_count = p.ws_bytes ? reinterpret_cast<int *>(ws) : nullptr;
+    a.ws_count = p.ws_bytes ? reinterpret_cast<uint64_t *>(ws) : nullptr;
     a.ws_rec = p.ws_bytes ? reinterpret_cast<float *>(ws + p.count_bytes) : nullptr;
     a.dtype = d->kv.dtype;
     a.out_f32 = (d->flags & PHOTON_DECODE_OUT_F32) ? 1 : 0;
     a.qscale = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    a.epoch = photon::next_epoch();
     hipError_t err = photon::launch_paged_multi_query(a, (hipStream_t)stream);
     if (err != hipSuccess)
         return fail(PHOTON_ERR_HIP, "multi-query launch: %s", hipGetErrorString(err));
@@ -470,7 +490,7 @@ photon_status decode_impl(const void *q, const void *k_new, const void *v_new, c
     if (workspace_bytes < p.ws_bytes)
         return fail(PHOTON_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
                     p.ws_bytes);
-    if (!workspace || !aligned16(workspace))
+    if (p.ws_bytes && (!workspace || !aligned16(workspace)))
         return fail(PHOTON_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
 
     photon::DecodeArgs a{};
@@ -483,8 +503,8 @@ photon_status decode_impl(const void *q, const void *k_new, const void *v_new, c
     a.context_lens = context_lens;
     a.out = out;
     char *ws = static_cast<char *>(workspace);
-    a.ws_count = reinterpret_cast<int *>(ws);
-    a.ws_rec = reinterpret_cast<float *>(ws + p.count_bytes);
+    a.ws_count = p.ws_bytes ? reinterpret_cast<uint64_t *>(ws) : nullptr;
+    a.ws_rec = p.ws_bytes ? reinterpret_cast<float *>(ws + p.count_bytes) : nullptr;
     a.num_seqs = desc->num_seqs;
     a.num_kv_heads = desc->kv.num_kv_heads;
     a.group = p.group;
@@ -495,6 +515,7 @@ photon_status decode_impl(const void *q, const void *k_new, const void *v_new, c
     a.max_blocks = desc->max_blocks_per_seq;
     a.num_waves = p.num_waves;
     a.qscale = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    a.epoch = photon::next_epoch();
     hipError_t err = photon::launch_paged_decode(a, (hipStream_t)stream);
     if (err != hipSuccess)
         return fail(PHOTON_ERR_HIP, "decode launch: %s", hipGetErrorString(err));

@@ -11,5 +11,7 @@ photon_status fail(photon_status st, const char *fmt, ...) __attribute__((format
 // Clear the detail message and return PHOTON_OK.
 photon_status ok();
 const char *last_detail();
+// Number of the next kernel call (never 0), the epoch of its arrival counters.
+uint32_t next_epoch();
 
 }  // namespace photon

@@ -138,10 +138,13 @@ def test_partition_quantum_and_auto_size():
 def test_workspace_size_formula():
     # 3 seqs x 2 KV heads x ceil(640/32) = 120 units; 2 units per wave -> 60 waves
     d = dd(b=3, hq=8, mb=40, maxctx=640, part=64, hkv=2)
-    counters = (3 * 2 * 4 + 255) // 256 * 256
+    counters = (3 * 2 * 8 + 255) // 256 * 256  # one 64-bit word per (sequence, KV head)
     record = (2 * 4 + 4 * 64) * 4
     assert pa.workspace_bytes(d) == counters + 60 * 2 * record
     assert pa.workspace_bytes(dd(b=0)) == 0
+    # contexts of at most one quantum are never split: no workspace at all
+    assert pa.workspace_bytes(dd(maxctx=32)) == 0
+    assert pa.workspace_bytes(dd(maxctx=33)) > 0
 
 
 @pytest.mark.parametrize("desc,code", [
@@ -267,7 +270,7 @@ def test_multi_query_split_and_workspace_formula():
     assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
     # automatic: 1024 / 32 = 32 splits wanted -> 4 blocks each, raised to the
     # fp32 per-tile minimum of 16 blocks -> ceil(125/16) = 8 splits
-    counters = (32 * 4 + 255) // 256 * 256
+    counters = (32 * 8 + 255) // 256 * 256  # one 64-bit word per tile
     rec = 16 * (64 + 2) * 4
     assert n.value == counters + 32 * 8 * rec
     # 16-bit storage: the 32-block minimum -> ceil(125/32) = 4 splits
@@ -277,7 +280,7 @@ def test_multi_query_split_and_workspace_formula():
     # fp32 with a query run of four tiles (the wide kernel): 32-block minimum
     dw = mqd(b=1, t=16, mq=16, mb=128, maxctx=2000)
     assert pa.lib.photon_paged_attn_multi_query_workspace_bytes(ctypes.byref(dw), ctypes.byref(n)) == 0
-    assert n.value == (8 * 4 + 255) // 256 * 256 + 8 * 4 * 4 * rec
+    assert n.value == (8 * 8 + 255) // 256 * 256 + 8 * 4 * 4 * rec
     d = mqd(mb=128, maxctx=2000)
     # explicit 512-token splits: 4 splits of 32 blocks
     d = mqd(mb=128, maxctx=2000, split=512)

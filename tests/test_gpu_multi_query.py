@@ -4,9 +4,10 @@ Tolerances as for the decode step: max-abs 1e-4 for fp32 output (fp32
 storage, or 16-bit storage with fp32 output: products are exact on the
 matrix cores and the softmax weights travel as a 16-bit value plus its
 rounding residual), 2e-3 for fp16 output, 1e-4 + 2^-8 |ref| for bfloat16
-output.  Large cases are checked on sampled rows: a row at position p
-equals the decode step over the first p + 1 tokens (a pinned property of
-the oracle).
+output.  Every output row is compared with the multi-query oracle, the
+512-row chunked prefill included; sampled rows of it are also compared with
+the decode oracle over the row's prefix (a row at position p equals the
+decode step over the first p + 1 tokens, a pinned property of the oracle).
 """
 import numpy as np
 import pytest
@@ -106,12 +107,16 @@ def test_speculative_verify_shape(pa, dtype):
     assert_close(got, ref, dtype, "speculative verify")
 
 
-def test_chunked_prefill_sampled_rows(pa):
+def test_chunked_prefill_every_row(pa):
     # four sequences, each computing a 512-token chunk of a longer prompt
+    # (1836 query rows); every row is compared with the multi-query oracle,
+    # and sampled rows also with the decode oracle over the row's prefix
     rng = np.random.default_rng(611)
     qlens, ctx = [512, 512, 300, 512], [2048, 512, 1500, 4000]
     q, kc, vc, tables, ctx, qs = ragged_case(rng, np.float16, qlens, ctx, 32, 8, 64, 16)
     got = gpu_mq(pa, q, kc, vc, tables, ctx, qs, 0.125)
+    ref = oracle.paged_attn_multi_query(q, kc, vc, tables, ctx, qs, 0.125)
+    assert_close(got, ref, np.float16, "chunked prefill, all rows")
     for b in range(4):
         for j in (0, 1, 255, qlens[b] - 1):
             row = qs[b] + j
@@ -191,12 +196,21 @@ def test_split_workspace_reused_stays_zeroed(pa):
         sizes[split] = pa.multi_query_workspace_bytes(d)
     assert all(v > 0 for v in sizes.values())
     ws = pa.new_workspace(max(sizes.values()), "cuda:0")
+    ws.zero_()
     tiles = 3 * 4 * ((9 * 4 + 15) // 16)
-    for rep in range(2):
+    for rep in range(3):
         for split in (64, 256, 0):
+            before = np.zeros(tiles, np.int64)
+            if rep == 2:  # arbitrary contents before the call (counters and records)
+                junk = rng.integers(0, 256, ws.numel(), dtype=np.uint8)
+                ws.copy_(torch.from_numpy(junk))
+                before = junk[: tiles * 8].view(np.int64)
             out = pa.paged_attn_multi_query(*args, 0.09, max_query_len=9, max_context_len=int(ctx.max()),
                                             workspace=ws, split_tokens=split)
             torch.cuda.synchronize()
             assert_close(di.from_torch(out), ref, np.float16, f"split {split} rep {rep}")
-            counters = ws[: tiles * 4].view(torch.int32).cpu().numpy()
-            assert (counters == 0).all()
+            # counters of split tiles are released to zero; the others are
+            # never touched
+            counters = ws[: tiles * 8].view(torch.int64).cpu().numpy()
+            assert ((counters == 0) | (counters == before)).all()
+            assert (counters == 0).any()

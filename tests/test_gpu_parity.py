@@ -128,17 +128,21 @@ def test_decode_matches_oracle_on_workloads(pa, name, layer):
     print(f"{name} layer {layer}: max-abs {err:.3e}")
 
 
-def test_decode_qwen3_long_sampled(pa):
-    # Full size (8 x 32768 tokens, fp16, d128); the oracle computes two sequences.
+def test_decode_qwen3_long_full(pa):
+    # The full-size Qwen3-shaped workload (8 x 32768 tokens, fp16, d128) in
+    # the launch configuration the benchmark uses (automatic partitioning,
+    # max_context_len = the longest context); every output element of all
+    # eight sequences is compared with the oracle (all host threads, a few
+    # seconds).
     cfg = di.CONFIGS["qwen3_long"]
     lay = di.make_layout(cfg)
     t = di.make_layer(cfg, lay)
     got = gpu_decode(pa, t.q, t.k_cache, t.v_cache, lay.block_tables, lay.context_lens, cfg.scale)
-    for b in (0, 5):
-        ref = oracle.paged_attn_decode(t.q[b:b + 1], t.k_cache, t.v_cache,
-                                       lay.block_tables[b:b + 1], lay.context_lens[b:b + 1],
-                                       cfg.scale)
-        err = assert_close(got[b:b + 1], ref, cfg.np_dtype, f"qwen3_long seq {b}")
+    ref = oracle.paged_attn_decode(t.q, t.k_cache, t.v_cache, lay.block_tables, lay.context_lens,
+                                   cfg.scale, num_threads=0)
+    assert got.shape == ref.shape == (8, 16, 128)
+    for b in range(8):
+        err = assert_close(got[b:b + 1], ref[b:b + 1], cfg.np_dtype, f"qwen3_long seq {b}")
         print(f"qwen3_long seq {b}: max-abs {err:.3e}")
 
 
@@ -269,8 +273,8 @@ def test_large_and_negative_scores(pa, scale):
 
 
 def test_workspace_reused_across_calls_stays_zeroed(pa):
-    # Arrival counters live at the start of the workspace; every call must
-    # leave them at zero so one workspace serves calls of any shape.
+    # Arrival counters live at the start of the workspace; every call that
+    # finishes leaves them at zero, and one workspace serves calls of any shape.
     rng = np.random.default_rng(27)
     q, kc, vc, tables, ctx = random_case(rng, np.float32, 9, 32, 8, 64, max_ctx=900)
     ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
@@ -280,14 +284,87 @@ def test_workspace_reused_across_calls_stays_zeroed(pa):
         desc = pa.decode_desc(args[0], args[1], args[3], int(ctx.max()), part)
         sizes[part] = pa.workspace_bytes(desc)
     ws = pa.new_workspace(max(sizes.values()), "cuda:0")
+    ws.zero_()
     for rep in range(2):
         for part in (32, 64, 128, 256):
             out = pa.paged_attn_decode(*args, 0.125, max_context_len=int(ctx.max()), workspace=ws,
                                        partition_tokens=part)
             torch.cuda.synchronize()
             assert_close(host(out), ref, np.float32, f"partition {part} rep {rep}")
-            counters = host(ws[: 9 * 8 * 4].view(torch.int32))
+            counters = host(ws[: 9 * 8 * 8].view(torch.int64))
             assert (counters == 0).all(), f"counters left at {counters[counters != 0]}"
+
+
+def _stale_patterns(n_words, rng):
+    """Counter contents a workspace may hold before a call: random words,
+    all ones, small counts with a zero tag, counts tagged with another call's
+    number (what a call that stopped early would leave), and a mix."""
+    tagged = (np.uint64(0x5A5A5A5A) << np.uint64(32)) | rng.integers(1, 40, n_words, dtype=np.uint64)
+    return {
+        "random": rng.integers(0, 2**64 - 1, n_words, dtype=np.uint64, endpoint=True),
+        "all_ones": np.full(n_words, np.uint64(2**64 - 1)),
+        "small_counts": rng.integers(1, 40, n_words, dtype=np.uint64),
+        "other_call": tagged,
+        "mixed": np.where(rng.random(n_words) < 0.5, tagged, np.uint64(0)),
+    }
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_workspace_contents_before_a_call_do_not_matter(pa, fused):
+    # Fill the whole workspace (counters and records) with arbitrary values
+    # before each call: the result must still match the oracle, and the call
+    # must leave every counter it used at zero.
+    rng = np.random.default_rng(28)
+    cfg = di.CONFIGS["cb_b64"]
+    lay = di.make_layout(cfg)
+    t = di.make_layer(cfg, lay)
+    if fused:
+        ek, ev = oracle.kv_cache_write(t.k_new, t.v_new, lay.slot_mapping, t.k_cache, t.v_cache)
+        ref = oracle.paged_attn_decode(t.q, ek, ev, lay.block_tables, lay.context_lens, cfg.scale)
+    else:
+        ref = oracle.paged_attn_decode(t.q, t.k_cache, t.v_cache, lay.block_tables,
+                                       lay.context_lens, cfg.scale)
+    q, tables, lens = dev(t.q), dev(lay.block_tables), dev(lay.context_lens)
+    kc0, vc0 = dev(t.k_cache), dev(t.v_cache)
+    for part in (0, 64):
+        desc = pa.decode_desc(q, kc0, tables, lay.max_context_len, part)
+        nbytes = pa.workspace_bytes(desc)
+        ws = pa.new_workspace(nbytes, "cuda:0")
+        n_words = 64 * 8  # one counter per (sequence, KV head)
+        for name, words in _stale_patterns(n_words, rng).items():
+            junk = rng.integers(0, 256, ws.numel(), dtype=np.uint8)
+            junk[: n_words * 8] = words.view(np.uint8)
+            ws.copy_(torch.from_numpy(junk))
+            before = words.view(np.int64)
+            kc, vc = kc0.clone(), vc0.clone()
+            if fused:
+                out = pa.paged_attn_decode_step(q, dev(t.k_new), dev(t.v_new), kc, vc, tables, lens,
+                                                cfg.scale, max_context_len=lay.max_context_len,
+                                                workspace=ws, partition_tokens=part)
+            else:
+                out = pa.paged_attn_decode(q, kc, vc, tables, lens, cfg.scale,
+                                           max_context_len=lay.max_context_len, workspace=ws,
+                                           partition_tokens=part)
+            torch.cuda.synchronize()
+            assert_close(host(out), ref, cfg.np_dtype, f"{name}, partition {part}")
+            # counters of split segments are released to zero; the others
+            # are never touched
+            counters = host(ws[: n_words * 8].view(torch.int64))
+            assert ((counters == 0) | (counters == before)).all(), name
+            assert (counters == 0).sum() >= 64, name
+
+
+def test_no_workspace_when_no_context_can_split(pa):
+    # max_context_len within one partition quantum: no segment is ever split,
+    # so the workspace query returns 0 and the call takes no workspace.
+    rng = np.random.default_rng(29)
+    q, kc, vc, tables, ctx = random_case(rng, np.float32, 40, 32, 8, 64, max_ctx=32)
+    desc = pa.decode_desc(dev(q), dev(kc), dev(tables), 32)
+    assert pa.partition_quantum(desc) == 32
+    assert pa.workspace_bytes(desc) == 0
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    got = gpu_decode(pa, q, kc, vc, tables, ctx, 0.125, max_ctx=32)
+    assert_close(got, ref, np.float32, "no workspace")
 
 
 def test_hip_graph_replays_match_eager(pa):
