@@ -328,6 +328,39 @@ PHOTON_API photon_status photon_paged_attn_decode(const void *q, const void *k_c
                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Size of the device array photon_paged_attn_decode_noalloc uses as its
+ * workspace (one copy per GPU the library runs on, held until the process
+ * ends).
+ */
+#define PHOTON_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * photon_paged_attn_decode without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it.  Same
+ * operation, arguments, kernels and results as photon_paged_attn_decode;
+ * the workspace is a static device array of PHOTON_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) per GPU, whose address is looked up once per device (on the
+ * first call that needs it, with that device current).
+ *
+ *   - stream must belong to the current device.
+ *   - A call whose workspace need (photon_paged_attn_workspace_bytes)
+ *     exceeds PHOTON_NOALLOC_SCRATCH_BYTES returns PHOTON_ERR_WORKSPACE and
+ *     launches nothing; every shape with automatic partitioning and
+ *     num_seqs * num_kv_heads up to a million fits.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     in time on one GPU (other streams, other threads) race and give wrong
+ *     results.  Calls on one stream are ordered and safe.  Nothing in the
+ *     array needs clearing between calls (see "Workspaces" above).
+ */
+PHOTON_API photon_status photon_paged_attn_decode_noalloc(const void *q, const void *k_cache,
+                                                          const void *v_cache,
+                                                          const int32_t *block_tables,
+                                                          const int32_t *context_lens, float scale,
+                                                          const photon_decode_desc *desc,
+                                                          void *out, void *stream);
+
+/*
  * One decode step in one launch: the cache write of each sequence's new
  * token fused with photon_paged_attn_decode (README "Technical details ->
  * Paged attention" and "GPU-optimised kernels").  For every sequence b with

@@ -40,6 +40,8 @@ DECODE_OUT_F32 = 1  # photon_decode_desc.flags: fp32 output for 16-bit storage
 
 BLOCK_SIZE = 16
 
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PHOTON_NOALLOC_SCRATCH_BYTES
+
 
 class PhotonError(RuntimeError):
     """A photon_* call returned a non-OK status."""
@@ -120,6 +122,9 @@ def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.photon_paged_attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                                   ctypes.POINTER(DecodeDesc), vp, vp, sz, vp]
     lib.photon_paged_attn_decode_step.restype = st
+    lib.photon_paged_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float,
+                                                     ctypes.POINTER(DecodeDesc), vp, vp]
+    lib.photon_paged_attn_decode_noalloc.restype = st
     lib.photon_status_str.argtypes = [st]
     lib.photon_status_str.restype = ctypes.c_char_p
     lib.photon_last_error_detail.argtypes = []
@@ -345,6 +350,34 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale: fl
                                        block_tables.data_ptr(), context_lens.data_ptr(),
                                        float(scale), ctypes.byref(desc), out.data_ptr(), ws_ptr,
                                        ws_len, _stream_ptr(q)))
+    return out
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                              max_context_len: int, out, partition_tokens: int = 0):
+    """:func:`paged_attn_decode` through the entry point that allocates
+    nothing: the library's static per-GPU scratch serves as the workspace,
+    and ``out`` (q's dtype, or float32) must be given, so the call makes no
+    allocation at all.  Calls that may overlap in time on one GPU race."""
+    import torch
+    _int32(block_tables=block_tables, context_lens=context_lens)
+    _args_ok(k_cache.device, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+             context_lens=context_lens, out=out)
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "q and pools differ")
+    if q.shape[2] != k_cache.shape[3] or block_tables.shape[0] != q.shape[0] \
+            or tuple(context_lens.shape) != (q.shape[0],) or out.shape != q.shape:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "shape mismatch")
+    if out.dtype not in (q.dtype, torch.float32):
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG",
+                          f"output dtype {out.dtype} is neither {q.dtype} nor float32")
+    flags = DECODE_OUT_F32 if out.dtype == torch.float32 and q.dtype != torch.float32 else 0
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens, flags)
+    with torch.cuda.device(q.device):  # the stream's device is the current one
+        check(get_lib().photon_paged_attn_decode_noalloc(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            context_lens.data_ptr(), float(scale), ctypes.byref(desc), out.data_ptr(),
+            _stream_ptr(q)))
     return out
 
 

@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 #include "photon_decode.h"
@@ -466,12 +467,47 @@ photon_status photon_paged_attn_workspace_bytes(const photon_decode_desc *desc, 
 
 }  // extern "C"
 
+// Workspace of photon_paged_attn_decode_noalloc: a fixed device array, one
+// copy per GPU, held until the process ends.  Host code never uses this name
+// as an address (on the host it is only a stand-in for the device symbol);
+// the device address of each GPU's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[PHOTON_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch` per device, once known
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current.
+photon_status current_device_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail(PHOTON_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(PHOTON_ERR_UNSUPPORTED, "device %d above the %d the scratch table holds", dev,
+                    kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !p)
+            return fail(PHOTON_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(err));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PHOTON_OK;
+}
 
 photon_status decode_impl(const void *q, const void *k_new, const void *v_new, const void *k_cache,
                           const void *v_cache, const int32_t *block_tables,
                           const int32_t *context_lens, float scale, const photon_decode_desc *desc,
-                          void *out, void *workspace, size_t workspace_bytes, void *stream)
+                          void *out, void *workspace, size_t workspace_bytes, void *stream,
+                          bool static_scratch = false)
 {
     Plan p;
     photon_status st = plan_decode(desc, &p);
@@ -487,6 +523,20 @@ photon_status decode_impl(const void *q, const void *k_new, const void *v_new, c
         return fail(PHOTON_ERR_INVALID_ARG, "block_tables and context_lens must be 4-byte aligned");
     if (!std::isfinite(scale))
         return fail(PHOTON_ERR_INVALID_ARG, "scale is not finite");
+    if (static_scratch) {
+        if (p.ws_bytes > (size_t)PHOTON_NOALLOC_SCRATCH_BYTES)
+            return fail(PHOTON_ERR_WORKSPACE,
+                        "this call needs %zu bytes of workspace, the static scratch holds %zu",
+                        p.ws_bytes, (size_t)PHOTON_NOALLOC_SCRATCH_BYTES);
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (p.ws_bytes) {  // first HIP call of the path, after every check
+            st = current_device_scratch(&workspace);
+            if (st != PHOTON_OK)
+                return st;
+            workspace_bytes = PHOTON_NOALLOC_SCRATCH_BYTES;
+        }
+    }
     if (workspace_bytes < p.ws_bytes)
         return fail(PHOTON_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
                     p.ws_bytes);
@@ -533,6 +583,16 @@ photon_status photon_paged_attn_decode(const void *q, const void *k_cache, const
 {
     return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale,
                        desc, out, workspace, workspace_bytes, stream);
+}
+
+photon_status photon_paged_attn_decode_noalloc(const void *q, const void *k_cache,
+                                               const void *v_cache, const int32_t *block_tables,
+                                               const int32_t *context_lens, float scale,
+                                               const photon_decode_desc *desc, void *out,
+                                               void *stream)
+{
+    return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale,
+                       desc, out, nullptr, 0, stream, true);
 }
 
 photon_status photon_paged_attn_decode_step(const void *q, const void *k_new, const void *v_new,

@@ -384,3 +384,21 @@ def test_binding_refuses_host_tensors(entry):
     torch = pytest.importorskip("torch")
     with pytest.raises(pa.PhotonError, match="GPU"):
         _binding_calls(torch, torch.int32)[entry]()
+
+
+def test_noalloc_decode_checks_before_any_hip_call():
+    m = re.search(r"#define PHOTON_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert pa.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+    def call(desc, q=FAKE, out=FAKE):
+        return pa.lib.photon_paged_attn_decode_noalloc(q, FAKE, FAKE, FAKE, FAKE, 0.125,
+                                                       ctypes.byref(desc), out, None)
+
+    # one wave per quantum over 2048 x 8 x 64 units: 2 GB of workspace
+    big = dd(b=2048, mb=128, maxctx=2048, part=32)
+    assert pa.workspace_bytes(big) > pa.NOALLOC_SCRATCH_BYTES
+    assert call(big) == pa.ERR_WORKSPACE
+    assert "scratch" in detail()
+    assert call(dd(), q=None) == pa.ERR_INVALID_ARG
+    assert call(dd(), out=FAKE + 4) == pa.ERR_INVALID_ARG
+    assert call(dd(b=0)) == pa.OK  # nothing to launch
