@@ -21,11 +21,24 @@ workload.  The fused rotary + cache-write kernel, the multi-query kernel and
 the host scheduler are timed after the step and reported in their own
 objects.
 
+``ceiling`` holds two bandwidth probes timed like the step's launches (HIP
+graph replay over the same pools): a bare gather of every valid K/V row of
+the call through the same block tables, with no arithmetic, and a plain
+streaming read of as many bytes; ``roofline.frac_of_ceiling`` is the
+gather's time over the decode's.  ``workloads`` gives one line per other
+configuration (batch 1, the ragged fp16 batch of 64, the Qwen3-shaped long
+context, bf16 at batch 16): time per fused call, algorithmic GB/s, fraction
+of 8 TB/s and of the gather ceiling of its own tables.
+
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload llama1b_b16]
+    python bench.py --summarize trace|pmc DIR --summary-command CMD   (no GPU: rocprofv3
+                                                                      output -> markdown)
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import functools
 import hashlib
 import json
 import os
@@ -33,6 +46,7 @@ import re
 import statistics
 import sys
 import time
+import warnings
 
 import numpy as np
 
@@ -43,7 +57,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["paged_attention_decode_photon_amd/csrc/paged_decode.hip",
                   "paged_attention_decode_photon_amd/csrc/lane_ops.h",
                   "paged_attention_decode_photon_amd/csrc/launch.h",
-                  "paged_attention_decode_photon_amd/csrc/elem.h"]
+                  "paged_attention_decode_photon_amd/csrc/elem.h",
+                  "paged_attention_decode_photon_amd/csrc/arrival.h"]
+# workloads reported one line each next to the headline
+SECONDARY_WORKLOADS = ["llama1b_b1", "cb_b64", "qwen3_long", "llama1b_b16_bf16"]
+TYPE_NAMES = {"f32": "float", "f16": "_Float16", "bf16": "__bf16"}
 
 
 def kernel_source_sha256() -> str:
@@ -54,15 +72,17 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_pmc.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_all_workloads_pmc.md")
+
+
+def measured_traffic(workload: str, path: str = PMC_SUMMARY):
+    """HBM bytes per decode launch of ``workload`` from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
-    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.]+)", text)
+    val = re.search(re.escape(workload) + r" hbm_bytes_per_launch:\s*([0-9.]+)", text)
     if not sha or not val or sha.group(1) != kernel_source_sha256():
         return None
     return float(val.group(1))
@@ -119,6 +139,18 @@ def parse_args(argv=None):
                          "device copy of known size, used to scale HBM byte counters)")
     ap.add_argument("--copy-bw-mib", type=int, default=1024,
                     help="size of the device-to-device copy timed for context (0 disables)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the bandwidth ceiling (streaming read and bare gather probes)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload lines of the other configurations")
+    ap.add_argument("--workloads", default=",".join(SECONDARY_WORKLOADS),
+                    help="comma-separated workloads measured besides the headline one")
+    ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIR"), default=None,
+                    help="no GPU work: summarise the rocprofv3 output under DIR (KIND 'trace' for "
+                         "a --kernel-trace --stats run, 'pmc' for counter runs, DIR may hold "
+                         "several) into markdown on stdout")
+    ap.add_argument("--summary-command", default="",
+                    help="the command that produced the rocprofv3 output (quoted in the summary)")
     ap.add_argument("--min-step-gib", type=float, default=1.0,
                     help="the workload's layers are replicated (fresh pools) until one step "
                          "reads at least this much distinct K/V, so no layer is served from "
@@ -520,8 +552,403 @@ def scheduler_measurements(trace_name: str = "serving"):
     }
 
 
+def time_graph(calls, stream, steps: int, warmup: int) -> dict:
+    """Per-call GPU time of ``calls`` (launch functions taking the HIP stream
+    to launch on).
+
+    The calls are captured once in a HIP graph (launched on the capturing
+    stream); each of ``steps`` replays is bracketed by events on ``stream``,
+    and the time per call is the replay's time over the number of calls
+    (host launch overhead excluded, back-to-back gaps included).
+    """
+    import torch
+    for c in calls:  # any first-use set-up happens outside the capture
+        c(stream.cuda_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with warnings.catch_warnings(record=True) as caught:
+        warnings.simplefilter("always")
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for c in calls:
+                c(cap)
+    if any("empty" in str(w.message) for w in caught):
+        raise RuntimeError("nothing was captured: the launches did not go to the capturing stream")
+    for _ in range(max(warmup, 1)):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    per = [a.elapsed_time(b) * 1e3 / len(calls) for a, b in ev]
+    p10, p90 = (float(x) for x in np.percentile(per, [10, 90]))
+    return {"us_mean": round(statistics.fmean(per), 3), "us_median": round(statistics.median(per), 3),
+            "us_p10_p90": [round(p10, 3), round(p90, 3)]}
+
+
+PROBE_WAVES = (1024, 2048, 4096, 8192)
+
+
+def gather_ceiling(pools, tables, lens, max_ctx: int, kv_bytes: int, stream, steps, warmup) -> dict:
+    """Bare gather of the decode call's K/V rows through its tables (no
+    arithmetic), over every (k_cache, v_cache) pair in ``pools``, one call
+    each per replay; the fastest wavefront count is the ceiling."""
+    import paged_attention_decode_photon_amd as pa
+    import torch
+    lib = pa.get_lib()
+    sink = torch.empty(max(PROBE_WAVES), dtype=torch.int32, device=tables.device)
+    desc = pa.DecodeDesc(lens.shape[0], pools[0][0].shape[1], tables.shape[1], max_ctx, 0,
+                         pa.kv_desc(pools[0][0]), 0)
+    dref = ctypes.byref(desc)
+    by_waves = {}
+    for waves in PROBE_WAVES:
+        calls = [functools.partial(_checked, lib.photon_probe_gather, kc.data_ptr(), vc.data_ptr(),
+                                   tables.data_ptr(), lens.data_ptr(), dref, waves,
+                                   sink.data_ptr()) for kc, vc in pools]
+        by_waves[waves] = time_graph(calls, stream, steps, warmup)["us_median"]
+    best = min(by_waves, key=by_waves.get)
+    us = by_waves[best]
+    return {"kernel": "gather_kernel (photon_probe_gather)", "bytes_per_call": kv_bytes,
+            "us_per_call_by_waves": {str(k): v for k, v in by_waves.items()}, "best_waves": best,
+            "us_per_call": us, "gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def stream_ceiling(nbytes: int, device, stream, steps, warmup, total_gib: float = 1.0) -> dict:
+    """Plain streaming read of ``nbytes`` per call, each call on a fresh
+    window of a buffer of at least ``total_gib`` GiB (so no window is served
+    from the 256 MiB Infinity Cache); the fastest wavefront count counts."""
+    import paged_attention_decode_photon_amd as pa
+    import torch
+    lib = pa.get_lib()
+    nbytes = (nbytes + 15) // 16 * 16
+    win = (nbytes + 4095) // 4096 * 4096
+    nwin = max(4, -(-int(total_gib * 2**30) // win))
+    buf = torch.zeros(nwin * win, dtype=torch.uint8, device=device)
+    sink = torch.empty(max(PROBE_WAVES), dtype=torch.int32, device=device)
+    by_waves = {}
+    for waves in PROBE_WAVES:
+        calls = [functools.partial(_checked, lib.photon_probe_stream_read, buf.data_ptr() + i * win,
+                                   nbytes, waves, sink.data_ptr()) for i in range(nwin)]
+        by_waves[waves] = time_graph(calls, stream, steps, warmup)["us_median"]
+    del buf
+    best = min(by_waves, key=by_waves.get)
+    us = by_waves[best]
+    return {"kernel": "stream_read_kernel (photon_probe_stream_read)", "bytes_per_call": nbytes,
+            "us_per_call_by_waves": {str(k): v for k, v in by_waves.items()}, "best_waves": best,
+            "us_per_call": us, "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def _checked(fn, *args):
+    import paged_attention_decode_photon_amd as pa
+    pa.check(fn(*args))
+
+
+def kv_read_bytes(cfg: di.DecodeConfig, ctx: np.ndarray) -> int:
+    """Bytes of the valid K and V rows of one decode call (what the probes read)."""
+    return int(np.asarray(ctx, dtype=np.int64).sum()) * cfg.num_kv_heads * cfg.head_dim \
+        * cfg.elem_bytes * 2
+
+
+def workload_line(name: str, device, stream, steps: int, warmup: int, min_gib: float,
+                  ceiling: bool = True) -> dict:
+    """One workload's fused decode step (append + decode, one launch per
+    call), timed per call by HIP-graph replay over copies of its pools that
+    add up to ``min_gib`` GiB (fresh data every call), next to the bare
+    gather of the same rows through the same tables.  The pools, q and new
+    rows are N(0,1) draws made on the GPU (torch, seeded with the
+    workload's seed); tables and contexts are the workload's own."""
+    import paged_attention_decode_photon_amd as pa
+    import torch
+    cfg = di.CONFIGS[name]
+    lay = di.make_layout(cfg)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg.seed)
+    b, hq, hkv, d = len(lay.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    pool_shape = (lay.num_blocks, hkv, cfg.block_size, d)
+    pool_bytes = 2 * lay.num_blocks * hkv * cfg.block_size * d * cfg.elem_bytes
+    copies = int(min(512, max(2, -(-int(min_gib * 2**30) // pool_bytes))))
+
+    def draw(shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(tdt)
+
+    layers = [{"q": draw((b, hq, d)), "kc": draw(pool_shape), "vc": draw(pool_shape),
+               "k": draw((b, hkv, d)), "v": draw((b, hkv, d))} for _ in range(copies)]
+    for L in layers:
+        L["out"] = torch.empty_like(L["q"])
+    tables = di.to_torch(lay.block_tables).to(device)
+    lens = di.to_torch(lay.context_lens).to(device)
+    max_ctx = lay.max_context_len
+    desc = pa.decode_desc(layers[0]["q"], layers[0]["kc"], tables, max_ctx)
+    ws_bytes = pa.workspace_bytes(desc)
+    ws = pa.new_workspace(ws_bytes, device)
+    lib, dref = pa.get_lib(), ctypes.byref(desc)
+    calls = [functools.partial(_checked, lib.photon_paged_attn_decode_step, L["q"].data_ptr(),
+                               L["k"].data_ptr(), L["v"].data_ptr(), L["kc"].data_ptr(),
+                               L["vc"].data_ptr(), tables.data_ptr(), lens.data_ptr(), cfg.scale,
+                               dref, L["out"].data_ptr(), ws.data_ptr(), ws_bytes)
+             for L in layers]
+    t = time_graph(calls, stream, steps, warmup)
+    n_written = int((lay.slot_mapping >= 0).sum())
+    nbytes = decode_bytes(cfg, lay.context_lens) + 4 * n_written * hkv * d * cfg.elem_bytes
+    us = t["us_median"]
+    line = {"config": {"batch": b, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
+                       "kv_dtype": cfg.dtype, "context_sum": int(lay.context_lens.sum()),
+                       "context_max": max_ctx, "pool_copies": copies},
+            "kernel": f"paged_decode_kernel<{TYPE_NAMES[cfg.dtype]}, {TYPE_NAMES[cfg.dtype]}, {d}, "
+                      f"{cfg.group}> (photon_paged_attn_decode_step)",
+            "bytes_per_call": nbytes, **t,
+            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tokens_per_s": round(b / (us * 1e-6), 1)}
+    if ceiling:
+        g = gather_ceiling([(L["kc"], L["vc"]) for L in layers], tables, lens, max_ctx,
+                           kv_read_bytes(cfg, lay.context_lens), stream, steps, warmup)
+        line["gather_ceiling"] = g
+        line["frac_of_gather_ceiling"] = round(g["us_per_call"] / us, 4)
+    del layers, ws
+    torch.cuda.empty_cache()
+    return line
+
+
+# ----------------------------------------------------------- profile summaries
+
+_MANGLED_TYPES = {"f": "float", "DF16_": "_Float16", "DF16b": "__bf16"}
+
+
+def decode_kernel_sig(name: str):
+    """(storage, output, head_dim, group) of a paged_decode_kernel dispatch
+    name, mangled or demangled; None for other kernels."""
+    m = re.search(r"paged_decode_kernel<\s*(\w+),\s*(\w+),\s*(\d+),\s*(\d+)\s*>", name)
+    if m:
+        return m.group(1), m.group(2), int(m.group(3)), int(m.group(4))
+    m = re.search(r"paged_decode_kernelI(f|DF16_|DF16b)(f|DF16_|DF16b)Li(\d+)ELi(\d+)E", name)
+    if m:
+        return (_MANGLED_TYPES[m.group(1)], _MANGLED_TYPES[m.group(2)], int(m.group(3)),
+                int(m.group(4)))
+    return None
+
+
+def short_kernel_name(name: str) -> str:
+    sig = decode_kernel_sig(name)
+    if sig:
+        return "paged_decode_kernel<%s, %s, %d, %d>" % sig
+    for key in ("gather_kernel", "stream_read_kernel", "paged_mq_wide_kernel", "paged_mq_kernel",
+                "kv_cache_write_kernel", "rope_kv_cache_write_kernel", "__amd_rocclr_copyBuffer"):
+        if key in name:
+            m = re.search(key + r"<([^>]*)>", name) or re.search(key + r"ILi(\d+)E", name)
+            return f"{key}<{m.group(1)}>" if m else key
+    return name[:60]
+
+
+def workload_dispatch_keys(names) -> dict:
+    """(decode kernel signature, grid threads) of each workload's fused-step
+    launch with automatic partitioning, from the library's own plan."""
+    import paged_attention_decode_photon_amd as pa
+    keys = {}
+    for name in names:
+        cfg = di.CONFIGS[name]
+        lay = di.make_layout(cfg)
+        desc = pa.DecodeDesc(len(lay.context_lens), cfg.num_q_heads, lay.max_blocks_per_seq,
+                             lay.max_context_len, 0,
+                             pa.KvDesc(lay.num_blocks, cfg.num_kv_heads, cfg.block_size,
+                                       cfg.head_dim, {"f32": pa.F32, "f16": pa.F16,
+                                                      "bf16": pa.BF16}[cfg.dtype]), 0)
+        t = TYPE_NAMES[cfg.dtype]
+        keys[name] = ((t, t, cfg.head_dim, cfg.group), planned_waves(desc) * 64)
+    return keys
+
+
+def planned_waves(desc) -> int:
+    """Wavefronts the library launches for ``desc`` with automatic
+    partitioning: one per unit of the largest batch the descriptor allows,
+    but no more than 256 compute units x max(4, 64 KiB / unit bytes), in
+    whole workgroups of four (the rule include/photon_decode.h states for
+    partition_tokens = 0; a CPU test checks it against the workspace size)."""
+    import paged_attention_decode_photon_amd as pa
+    quantum = pa.partition_quantum(desc)
+    eb = 4 if desc.kv.dtype == pa.F32 else 2
+    chunks = -(-desc.max_context_len // quantum)
+    upper = desc.num_seqs * desc.kv.num_kv_heads * chunks
+    per_cu = max(4, (64 * 1024) // (2 * quantum * desc.kv.head_dim * eb))
+    waves = max(1, min(upper, 256 * per_cu))
+    return -(-waves // 4) * 4
+
+
+def _read_csvs(root: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _col(row: dict, *names):
+    for n in names:
+        if n in row and row[n] != "":
+            return row[n]
+    raise KeyError(names)
+
+
+def summarize_trace(root: str, command: str) -> str:
+    """Markdown summary of a rocprofv3 --kernel-trace run: per-kernel
+    durations, the decode kernel split by workload (signature and grid), its
+    algorithmic GB/s and its fraction of the gather probe's rate."""
+    rows = _read_csvs(root, "kernel_trace.csv")
+    if not rows:
+        raise SystemExit(f"no *kernel_trace.csv under {root}")
+    groups: dict = {}
+    for r in rows:
+        name = _col(r, "Kernel_Name")
+        grid = int(_col(r, "Grid_Size_X", "Grid_Size"))
+        dur = (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3
+        groups.setdefault((short_kernel_name(name), grid), []).append(dur)
+    total = sum(sum(v) for v in groups.values())
+    out = ["# Kernel durations (rocprofv3 kernel trace): decode on every workload, the bandwidth "
+           "probes and the other kernels the benchmark runs", "",
+           "Command ($REPO is the repository root):", "",
+           "```", command, "```", "",
+           "| kernel | grid (threads) | calls | average (us) | median (us) | min (us) | max (us) | share |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {name} | {grid} | {len(v)} | {statistics.fmean(v):.2f} | "
+                   f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                   f"{100 * sum(v) / total:.1f}% |")
+    out.append("")
+    keys = workload_dispatch_keys(list(di.CONFIGS))
+    gathers = {g: statistics.median(v) for (n, g), v in groups.items() if n.startswith("gather")}
+    out += ["Decode kernel by workload (fused append + decode launches; algorithmic bytes as in "
+            "`bench.decode_bytes` plus the new rows read and appended):", "",
+            "| workload | launches | average (us) | median (us) | bytes per launch | GB/s at the average "
+            "| % of 8 TB/s |", "|---|---|---|---|---|---|---|"]
+    for wl, (sig, grid) in keys.items():
+        v = [d for (n, g), ds in groups.items() for d in ds
+             if g == grid and n == "paged_decode_kernel<%s, %s, %d, %d>" % sig]
+        if not v:
+            continue
+        cfg = di.CONFIGS[wl]
+        lay = di.make_layout(cfg)
+        nbytes = decode_bytes(cfg, lay.context_lens) + 4 * int((lay.slot_mapping >= 0).sum()) \
+            * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+        avg = statistics.fmean(v)
+        gbps = nbytes / (avg * 1e-6) / 1e9
+        out.append(f"| {wl} | {len(v)} | {avg:.2f} | {statistics.median(v):.2f} | {nbytes} | "
+                   f"{gbps:.1f} | {100 * gbps / HBM_PEAK_GBPS:.1f}% |")
+        out.append(f"<!-- {wl} decode_avg_us: {avg:.3f} -->")
+    if gathers:
+        out += ["", "Gather probe launches (median us by grid size): " +
+                ", ".join(f"{g // 64} waves: {u:.2f}" for g, u in sorted(gathers.items()))]
+    out += ["", f"kernel_source_sha256: {kernel_source_sha256()}"]
+    return "\n".join(out) + "\n"
+
+
+def summarize_pmc(root: str, command: str) -> str:
+    """Markdown summary of rocprofv3 --pmc runs under ``root`` (one
+    subdirectory per pass): every counter's mean per dispatch for the decode
+    kernel of each workload, and HBM bytes from FETCH_SIZE / WRITE_SIZE
+    scaled by what the same counters read for a copy of known size."""
+    rows = _read_csvs(root, "counter_collection.csv")
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {root}")
+    per: dict = {}
+    for r in rows:
+        name = short_kernel_name(_col(r, "Kernel_Name"))
+        grid = int(_col(r, "Grid_Size", "Grid_Size_X"))
+        key = (name, grid, _col(r, "Counter_Name"))
+        disp = _col(r, "Dispatch_Id", "Correlation_Id")
+        per.setdefault(key, {}).setdefault(disp, 0.0)
+        per[key][disp] += float(_col(r, "Counter_Value"))
+    mean = {k: statistics.fmean(v.values()) for k, v in per.items()}
+    ndisp = {k: len(v) for k, v in per.items()}
+    counters = sorted({k[2] for k in per})
+    out = ["# Decode kernel counters on every workload (rocprofv3 --pmc)", "",
+           "Counter passes, one run each ($REPO is the repository root); the passes were "
+           "FETCH_SIZE | WRITE_SIZE | TCC_HIT_sum TCC_MISS_sum | OccupancyPercent "
+           "MeanOccupancyPerCU LDSBankConflict | SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
+           "SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_VMEM_RD | "
+           "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_INSTS_SALU "
+           "SQ_INSTS_MFMA SQ_ACTIVE_INST_LDS SQ_INSTS_SMEM:", "", "```", command, "```", ""]
+    # copy calibration: the largest copyBuffer dispatch is the known-size copy
+    scale = {}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        cands = [(g, mean[(n, g, c)]) for (n, g, c) in mean if n == "__amd_rocclr_copyBuffer"
+                 and c == cname]
+        if cands:
+            g, kib = max(cands)
+            copy_bytes = COPY_CALIBRATION_BYTES
+            scale[cname] = copy_bytes / (kib * 1024.0)
+            out.append(f"Calibration: a copy of {copy_bytes} bytes reads {cname} = {kib:.1f} KiB "
+                       f"per dispatch; scale {scale[cname]:.5f}.")
+    out.append("")
+    keys = workload_dispatch_keys(list(di.CONFIGS))
+    for wl, (sig, grid) in keys.items():
+        name = "paged_decode_kernel<%s, %s, %d, %d>" % sig
+        have = [c for c in counters if (name, grid, c) in mean]
+        if not have:
+            continue
+        cfg = di.CONFIGS[wl]
+        lay = di.make_layout(cfg)
+        nbytes = decode_bytes(cfg, lay.context_lens) + 4 * int((lay.slot_mapping >= 0).sum()) \
+            * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+        out += [f"### {wl}: {name}, {grid // 64} wavefronts", "",
+                "| counter | mean per dispatch | dispatches |", "|---|---|---|"]
+        for c in have:
+            out.append(f"| {c} | {mean[(name, grid, c)]:.1f} | {ndisp[(name, grid, c)]} |")
+        if all((name, grid, c) in mean for c in ("FETCH_SIZE", "WRITE_SIZE")) and len(scale) == 2:
+            hbm = mean[(name, grid, "FETCH_SIZE")] * 1024 * scale["FETCH_SIZE"] + \
+                mean[(name, grid, "WRITE_SIZE")] * 1024 * scale["WRITE_SIZE"]
+            out += ["", f"Algorithmic bytes per launch {nbytes}; HBM bytes per launch (scaled) "
+                    f"{hbm:.0f} = {hbm / nbytes:.3f} x algorithmic.",
+                    f"<!-- {wl} hbm_bytes_per_launch: {hbm:.0f} -->"]
+        if (name, grid, "TCC_HIT_sum") in mean and (name, grid, "TCC_MISS_sum") in mean:
+            h, m = mean[(name, grid, "TCC_HIT_sum")], mean[(name, grid, "TCC_MISS_sum")]
+            out.append(f"L2 hit rate {100 * h / max(h + m, 1):.1f}%.")
+        if (name, grid, "SQ_WAVE_CYCLES") in mean:
+            # SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_* count per-wave
+            # quad-cycles, so their ratios are fractions of wave lifetime
+            wc = mean[(name, grid, "SQ_WAVE_CYCLES")]
+            for c, what in (("SQ_ACTIVE_INST_VALU", "issuing VALU instructions"),
+                            ("SQ_WAIT_INST_ANY", "waiting for a dependency (s_waitcnt)"),
+                            ("SQ_WAIT_ANY", "waiting for anything")):
+                if (name, grid, c) in mean:
+                    out.append(f"{c} / SQ_WAVE_CYCLES = {mean[(name, grid, c)] / wc:.3f} "
+                               f"(share of wave time {what}).")
+            if (name, grid, "SQ_WAVES") in mean:
+                nw = mean[(name, grid, "SQ_WAVES")]
+                out.append(f"Mean wave lifetime {4 * wc / nw / 2.4e3:.2f} us at 2.4 GHz "
+                           f"({nw:.0f} waves).")
+                if (name, grid, "SQ_INSTS_VALU") in mean:
+                    out.append(f"VALU instructions per wave {mean[(name, grid, 'SQ_INSTS_VALU')] / nw:.0f}.")
+        if (name, grid, "SQ_LDS_BANK_CONFLICT") in mean and (name, grid, "SQ_LDS_IDX_ACTIVE") in mean:
+            out.append("LDS bank conflict cycles / LDS active cycles = "
+                       f"{mean[(name, grid, 'SQ_LDS_BANK_CONFLICT')] / max(mean[(name, grid, 'SQ_LDS_IDX_ACTIVE')], 1):.3f}.")
+        out.append("")
+    out += [f"kernel_source_sha256: {kernel_source_sha256()}"]
+    return "\n".join(out) + "\n"
+
+
+COPY_CALIBRATION_BYTES = 256 << 20  # --calibrate-copy-mib 256 in the counter runs
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
+    if args.summarize:
+        kind, root = args.summarize
+        if kind not in ("trace", "pmc"):
+            print("--summarize KIND must be 'trace' or 'pmc'", file=sys.stderr)
+            return 2
+        fn = summarize_trace if kind == "trace" else summarize_pmc
+        sys.stdout.write(fn(root, args.summary_command))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(every (sequence, KV head) pair is independent, see the sharding notes)",
@@ -682,20 +1109,38 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     single_us = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in single)
 
+    ceiling = None
+    if not args.no_ceiling:
+        kvb = kv_read_bytes(cfg, lay.context_lens)
+        ceiling = {"gather": gather_ceiling([(L["kc"], L["vc"]) for L in layers], tables, lens,
+                                            max_ctx, kvb, stream, args.steps, args.warmup),
+                   "stream_read": stream_ceiling(kvb, device, stream, args.steps, args.warmup)}
     rope = rope_measurements(args, cfg, lay, layers, slots, device, stream) \
         if args.rope_prefill_tokens > 0 else None
     mq = None if args.no_multi_query else \
         multi_query_measurements(args, cfg, lay, layers, device, stream)
+
+    workloads = None
+    if not args.no_workloads:
+        del layers[:]  # free the headline pools before the other workloads'
+        torch.cuda.empty_cache()
+        workloads = {}
+        for name in [w for w in args.workloads.split(",") if w and w != cfg.name]:
+            workloads[name] = workload_line(name, device, stream, args.steps, args.warmup,
+                                            args.min_step_gib, ceiling=not args.no_ceiling)
+            print(f"workload {name}: {workloads[name]['us_median']} us per call", file=sys.stderr,
+                  flush=True)
 
     per_decode = decode_bytes(cfg, lay.context_lens)
     n_written = int((lay.slot_mapping >= 0).sum())
     # the fused launch also reads each new K/V row and writes it to the pool
     per_append = 4 * n_written * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
     per_launch = per_decode + per_append
-    step_bytes = len(layers) * per_launch
+    n_launch = len(host_layers) * copies
+    step_bytes = n_launch * per_launch
     value = step_bytes / (step_ms * 1e-3) / 1e9
     achieved = per_launch / (call_mean * 1e-6) / 1e9
-    tok_per_layer = len(lay.context_lens) / (step_ms * 1e-3 / len(layers))
+    tok_per_layer = len(lay.context_lens) / (step_ms * 1e-3 / n_launch)
 
     result = {
         "metric": "decode attention KV GB/s (% of HBM peak) + tokens/s per layer at batch 16",
@@ -713,7 +1158,7 @@ def main(argv=None) -> int:
         "config": {
             "workload": cfg.name,
             "batch": len(lay.context_lens),
-            "layers_per_step": len(layers),
+            "layers_per_step": n_launch,
             "num_q_heads": cfg.num_q_heads,
             "num_kv_heads": cfg.num_kv_heads,
             "head_dim": cfg.head_dim,
@@ -748,6 +1193,21 @@ def main(argv=None) -> int:
             "bytes_per_launch": per_launch,
         },
     }
+    if ceiling is not None:
+        # decode against the bare gather of the same rows through the same
+        # tables, both timed per call by graph replay over the same pools
+        dec_us = step_ms * 1e3 / n_launch
+        g = ceiling["gather"]
+        ceiling["decode_us_per_call_graph"] = round(dec_us, 3)
+        ceiling["decode_frac_of_gather_ceiling"] = round(g["us_per_call"] / dec_us, 4)
+        ceiling["note"] = ("gather: every valid K/V row of the call through the block tables, "
+                           "no arithmetic; stream_read: the same number of bytes from one "
+                           "contiguous buffer; fraction = gather time / decode time per call")
+        result["roofline"]["ceiling_gbps"] = g["gbps"]
+        result["roofline"]["frac_of_ceiling"] = round(g["us_per_call"] / dec_us, 4)
+        result["ceiling"] = ceiling
+    if workloads is not None:
+        result["workloads"] = workloads
     if rope is not None:
         result["rope_kv_cache_write"] = rope
     if mq is not None:

@@ -125,6 +125,10 @@ def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.photon_paged_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float,
                                                      ctypes.POINTER(DecodeDesc), vp, vp]
     lib.photon_paged_attn_decode_noalloc.restype = st
+    lib.photon_probe_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.photon_probe_stream_read.restype = st
+    lib.photon_probe_gather.argtypes = [vp, vp, vp, vp, ctypes.POINTER(DecodeDesc), i32, vp, vp]
+    lib.photon_probe_gather.restype = st
     lib.photon_status_str.argtypes = [st]
     lib.photon_status_str.restype = ctypes.c_char_p
     lib.photon_last_error_detail.argtypes = []
@@ -490,3 +494,37 @@ def paged_attn_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, cont
                                             float(scale), ctypes.byref(desc), out.data_ptr(),
                                             ws_ptr, ws_len, _stream_ptr(q)))
     return out
+
+
+def probe_stream_read(buf, waves: int, sink=None):
+    """Bandwidth probe: read every byte of ``buf`` (a contiguous GPU tensor)
+    with ``waves`` wavefronts, no arithmetic.  Returns the uint32 ``sink``
+    of per-wavefront XORs of the 32-bit words read (include/photon_probe.h)."""
+    import torch
+    _args_ok(buf.device, buf=buf)
+    if sink is None:
+        sink = torch.empty(waves, dtype=torch.int32, device=buf.device)
+    check(get_lib().photon_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                             int(waves), sink.data_ptr(), _stream_ptr(buf)))
+    return sink
+
+
+def probe_gather(k_cache, v_cache, block_tables, context_lens, max_context_len: int, waves: int,
+                 sink=None):
+    """Bandwidth probe: read every valid K and V row of the decode call over
+    these tables and lengths, split evenly over ``waves`` wavefronts, no
+    arithmetic.  Returns the per-wavefront XORs (include/photon_probe.h)."""
+    import torch
+    _int32(block_tables=block_tables, context_lens=context_lens)
+    _args_ok(k_cache.device, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+             context_lens=context_lens)
+    hkv = k_cache.shape[1]
+    desc = DecodeDesc(context_lens.shape[0], hkv, block_tables.shape[1], int(max_context_len), 0,
+                      kv_desc(k_cache), 0)
+    if sink is None:
+        sink = torch.empty(waves, dtype=torch.int32, device=k_cache.device)
+    check(get_lib().photon_probe_gather(k_cache.data_ptr(), v_cache.data_ptr(),
+                                        block_tables.data_ptr(), context_lens.data_ptr(),
+                                        ctypes.byref(desc), int(waves), sink.data_ptr(),
+                                        _stream_ptr(k_cache)))
+    return sink

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libphoton_decode.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["photon_abi.hip", "kv_cache_write.hip", "paged_decode.hip", "rope_kv_write.hip",
-           "paged_multi_query.hip"]
+           "paged_multi_query.hip", "bandwidth_probe.hip"]
 HOST_SOURCES = ["scheduler.cpp"]  # host-only C++ (the block manager and scheduler)
 ARCH = "gfx950"
 

@@ -402,3 +402,30 @@ def test_noalloc_decode_checks_before_any_hip_call():
     assert call(dd(), q=None) == pa.ERR_INVALID_ARG
     assert call(dd(), out=FAKE + 4) == pa.ERR_INVALID_ARG
     assert call(dd(b=0)) == pa.OK  # nothing to launch
+
+
+def test_probes_validate_before_any_hip_call():
+    lib = pa.lib
+
+    def stream(buf=FAKE, nbytes=1 << 20, waves=64, sink=FAKE):
+        return lib.photon_probe_stream_read(buf, nbytes, waves, sink, None)
+
+    assert stream(waves=0) == pa.ERR_INVALID_ARG
+    assert stream(waves=6) == pa.ERR_INVALID_ARG          # not whole workgroups
+    assert stream(waves=(1 << 20) + 4) == pa.ERR_INVALID_ARG
+    assert stream(sink=None) == pa.ERR_INVALID_ARG
+    assert stream(buf=None) == pa.ERR_INVALID_ARG
+    assert stream(buf=FAKE + 8) == pa.ERR_INVALID_ARG
+    assert stream(nbytes=0) == pa.ERR_INVALID_ARG
+    assert stream(nbytes=24) == pa.ERR_INVALID_ARG
+    assert stream(nbytes=1 << 40, waves=4) == pa.ERR_UNSUPPORTED
+
+    def gather(desc, kc=FAKE, waves=64):
+        return lib.photon_probe_gather(kc, FAKE, FAKE, FAKE, ctypes.byref(desc), waves, FAKE, None)
+
+    assert gather(dd(b=65)) == pa.ERR_UNSUPPORTED        # prefix sums of at most 64 sequences
+    assert gather(dd(bs=32)) == pa.ERR_UNSUPPORTED
+    assert gather(dd(dtype=7)) == pa.ERR_INVALID_ARG
+    assert gather(dd(maxctx=128 * 16 + 1)) == pa.ERR_INVALID_ARG
+    assert gather(dd(), kc=None) == pa.ERR_INVALID_ARG
+    assert gather(dd(), waves=3) == pa.ERR_INVALID_ARG

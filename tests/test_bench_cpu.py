@@ -47,12 +47,15 @@ def test_recorded_traffic_is_used_only_for_the_current_source(tmp_path, monkeypa
         dst.write_bytes(open(os.path.join(ROOT, rel), "rb").read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     sha = bench.kernel_source_sha256()
-    f = prof / "paged_decode_w_pmc.md"
-    f.write_text(f"hbm_bytes_per_launch: 1234\nkernel_source_sha256: {sha}\n")
-    assert bench.measured_traffic("w") == 1234.0
-    f.write_text("hbm_bytes_per_launch: 1234\nkernel_source_sha256: " + "0" * 64 + "\n")
-    assert bench.measured_traffic("w") is None
-    assert bench.measured_traffic("absent") is None
+    f = prof / "summary_pmc.md"
+    f.write_text(f"<!-- w hbm_bytes_per_launch: 1234 -->\n<!-- v hbm_bytes_per_launch: 99 -->\n"
+                 f"kernel_source_sha256: {sha}\n")
+    assert bench.measured_traffic("w", str(f)) == 1234.0
+    assert bench.measured_traffic("v", str(f)) == 99.0
+    assert bench.measured_traffic("absent", str(f)) is None
+    f.write_text("<!-- w hbm_bytes_per_launch: 1234 -->\nkernel_source_sha256: " + "0" * 64 + "\n")
+    assert bench.measured_traffic("w", str(f)) is None
+    assert bench.measured_traffic("w", str(prof / "missing.md")) is None
 
 
 def test_more_than_one_gpu_is_refused():
@@ -61,3 +64,34 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_planned_waves_matches_the_workspace_size():
+    # the summariser's copy of the automatic wave rule must agree with the
+    # library: the decode workspace holds two records per wavefront
+    import paged_attention_decode_photon_amd as pa
+    import bench
+    for name, cfg in di.CONFIGS.items():
+        lay = di.make_layout(cfg)
+        desc = pa.DecodeDesc(len(lay.context_lens), cfg.num_q_heads, lay.max_blocks_per_seq,
+                             lay.max_context_len, 0,
+                             pa.KvDesc(lay.num_blocks, cfg.num_kv_heads, cfg.block_size,
+                                       cfg.head_dim, {"f32": pa.F32, "f16": pa.F16,
+                                                      "bf16": pa.BF16}[cfg.dtype]), 0)
+        ws = pa.workspace_bytes(desc)
+        if ws == 0:
+            continue
+        counters = (len(lay.context_lens) * cfg.num_kv_heads * 8 + 255) // 256 * 256
+        rec = ((2 * cfg.group + cfg.group * cfg.head_dim + 3) & ~3) * 4
+        assert (ws - counters) == bench.planned_waves(desc) * 2 * rec, name
+
+
+def test_decode_kernel_names_parse_in_both_forms():
+    import bench
+    assert bench.decode_kernel_sig("_ZN6photon12_GLOBAL__N_119paged_decode_kernelIDF16bDF16bLi64ELi4EEEvNS0_10KernelArgsE") \
+        == ("__bf16", "__bf16", 64, 4)
+    assert bench.decode_kernel_sig("_ZN6photon12_GLOBAL__N_119paged_decode_kernelIDF16_fLi128ELi2EEEvNS0_10KernelArgsE") \
+        == ("_Float16", "float", 128, 2)
+    assert bench.decode_kernel_sig("void photon::(anonymous namespace)::paged_decode_kernel<float, float, 64, 4>(photon::(anonymous namespace)::KernelArgs)") \
+        == ("float", "float", 64, 4)
+    assert bench.decode_kernel_sig("paged_mq_kernel<float, float, 64, 4>") is None
