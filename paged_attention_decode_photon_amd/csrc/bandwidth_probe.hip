@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 #include "elem.h"
+#include "lane_ops.h"
 #include "photon_probe.h"
 #include "status.h"
 
@@ -112,13 +113,7 @@ __global__ __launch_bounds__(kProbeWaves * 64) void gather_kernel(GatherArgs a)
     // Tiles per sequence (Hkv * blocks), prefix-summed across lanes.
     const int cl = lane < B ? a.context_lens[lane] : 0;
     const int nb = (cl + 15) / 16;
-    int end = hkv * nb;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int n = __shfl_up(end, d, 64);
-        if (lane >= d)
-            end += n;
-    }
+    const int end = wave_inclusive_sum(hkv * nb);
     const int total = B > 0 ? __builtin_amdgcn_readlane(end, B - 1) : 0;
     const int u0 = (int)((int64_t)wave * total / a.num_waves);
     const int u1 = (int)((int64_t)(wave + 1) * total / a.num_waves);

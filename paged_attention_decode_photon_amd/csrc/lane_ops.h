@@ -88,4 +88,29 @@ __device__ __forceinline__ float read_lane(float v, int lane)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// DPP controls of the wave-wide scan below (gfx9-family encodings).
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+// Inclusive prefix sum over the 64 lanes of a wave.  Inside each 16-lane
+// row a log-step scan with row_shr 1, 2, 4, 8 (a lane with no source in its
+// row adds 0); then row_bcast:15 adds the total of row r to row r + 1 (rows
+// 1 and 3 written), and row_bcast:31 adds the total of rows 0-1 to rows 2
+// and 3.  Six DPP adds and no LDS traffic, where a shuffle-based scan costs
+// six serialised LDS permutes.
+__device__ __forceinline__ int wave_inclusive_sum(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false);
+    return v;
+}
+
 }  // namespace photon

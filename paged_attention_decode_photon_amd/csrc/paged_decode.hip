@@ -656,15 +656,8 @@ __device__ int2 block_inclusive_scan2(int2 v, int2 *wave_totals)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int nx = __shfl_up(v.x, d, 64);
-        const int ny = __shfl_up(v.y, d, 64);
-        if (lane >= d) {
-            v.x += nx;
-            v.y += ny;
-        }
-    }
+    v.x = wave_inclusive_sum(v.x);
+    v.y = wave_inclusive_sum(v.y);
     if (lane == 63)
         wave_totals[wave] = v;
     __syncthreads();
@@ -705,27 +698,25 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     int r_ctx = 0, r_end = 0, r_ne = 0;
     if (small) {
         const int cl = lane < B ? a.context_lens[lane] : 0;
-        int u = hkv * ((cl + CT - 1) / CT), n = cl > 0 ? 1 : 0;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int nu = __shfl_up(u, d, 64);
-            const int nn = __shfl_up(n, d, 64);
-            if (lane >= d) {
-                u += nu;
-                n += nn;
-            }
-        }
         r_ctx = cl;
-        r_end = u;
-        r_ne = n;
+        r_end = wave_inclusive_sum(hkv * ((cl + CT - 1) / CT));
+        r_ne = wave_inclusive_sum(cl > 0 ? 1 : 0);
     } else {
+        // Each thread owns `per` consecutive sequences; their lengths are
+        // all loaded before any is used (one round trip, not `per`).
+        constexpr int kMaxPer = (kMaxDecodeSeqs + NT - 1) / NT;
         const int per = (B + NT - 1) / NT;
         const int first = threadIdx.x * per;
+        int cls[kMaxPer];
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j)
+            cls[j] = (j < per && first + j < B) ? a.context_lens[first + j] : 0;
         int2 mine = make_int2(0, 0);
-        for (int j = 0; j < per; ++j) {
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) {
             const int bb = first + j;
-            if (bb < B) {
-                const int cl = a.context_lens[bb];
+            if (j < per && bb < B) {
+                const int cl = cls[j];
                 ctx_lds[bb] = cl;
                 mine.x += hkv * ((cl + CT - 1) / CT);
                 mine.y += cl > 0 ? 1 : 0;
@@ -734,10 +725,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         int2 run = block_inclusive_scan2(mine, wave_totals);
         run.x -= mine.x;
         run.y -= mine.y;
-        for (int j = 0; j < per; ++j) {
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) {
             const int bb = first + j;
-            if (bb < B) {
-                const int cl = ctx_lds[bb];
+            if (j < per && bb < B) {
+                const int cl = cls[j];
                 run.x += hkv * ((cl + CT - 1) / CT);
                 run.y += cl > 0 ? 1 : 0;
                 unit_end[bb] = run.x;
@@ -808,6 +800,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     int b;
     if (small) {
         b = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < B && r_end + C * hkv * r_ne > v_begin));
+        b = b < B ? b : B - 1;  // (v_begin < total_v, so some lane qualifies)
     } else {
         const int step = (B + 63) / 64;
         const int grp = __builtin_ctzll(__builtin_amdgcn_ballot_w64(
