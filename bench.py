@@ -151,6 +151,9 @@ def parse_args(argv=None):
                          "several) into markdown on stdout")
     ap.add_argument("--summary-command", default="",
                     help="the command that produced the rocprofv3 output (quoted in the summary)")
+    ap.add_argument("--summary-workload", default=None, choices=sorted(di.CONFIGS),
+                    help="with --summarize trace: the run measured only this workload, so its "
+                         "probe launches are this workload's ceiling")
     ap.add_argument("--min-step-gib", type=float, default=1.0,
                     help="the workload's layers are replicated (fresh pools) until one step "
                          "reads at least this much distinct K/V, so no layer is served from "
@@ -740,8 +743,9 @@ def short_kernel_name(name: str) -> str:
     sig = decode_kernel_sig(name)
     if sig:
         return "paged_decode_kernel<%s, %s, %d, %d>" % sig
+    # longer names first: "rope_kv_cache_write_kernel" contains "kv_cache_write_kernel"
     for key in ("gather_kernel", "stream_read_kernel", "paged_mq_wide_kernel", "paged_mq_kernel",
-                "kv_cache_write_kernel", "rope_kv_cache_write_kernel", "__amd_rocclr_copyBuffer"):
+                "rope_kv_cache_write_kernel", "kv_cache_write_kernel", "__amd_rocclr_copyBuffer"):
         if key in name:
             m = re.search(key + r"<([^>]*)>", name) or re.search(key + r"ILi(\d+)E", name)
             return f"{key}<{m.group(1)}>" if m else key
@@ -799,10 +803,11 @@ def _col(row: dict, *names):
     raise KeyError(names)
 
 
-def summarize_trace(root: str, command: str) -> str:
+def summarize_trace(root: str, command: str, workload: str | None = None) -> str:
     """Markdown summary of a rocprofv3 --kernel-trace run: per-kernel
-    durations, the decode kernel split by workload (signature and grid), its
-    algorithmic GB/s and its fraction of the gather probe's rate."""
+    durations, the decode kernel split by workload (signature and grid) with
+    its algorithmic GB/s; for a run of one ``workload``, also its bandwidth
+    probes and the decode's fraction of the fastest gather."""
     rows = _read_csvs(root, "kernel_trace.csv")
     if not rows:
         raise SystemExit(f"no *kernel_trace.csv under {root}")
@@ -826,6 +831,8 @@ def summarize_trace(root: str, command: str) -> str:
     out.append("")
     keys = workload_dispatch_keys(list(di.CONFIGS))
     gathers = {g: statistics.median(v) for (n, g), v in groups.items() if n.startswith("gather")}
+    if workload is None:
+        gathers = {}  # several workloads' probes share kernels and grids
     out += ["Decode kernel by workload (fused append + decode launches; algorithmic bytes as in "
             "`bench.decode_bytes` plus the new rows read and appended):", "",
             "| workload | launches | average (us) | median (us) | bytes per launch | GB/s at the average "
@@ -844,9 +851,30 @@ def summarize_trace(root: str, command: str) -> str:
         out.append(f"| {wl} | {len(v)} | {avg:.2f} | {statistics.median(v):.2f} | {nbytes} | "
                    f"{gbps:.1f} | {100 * gbps / HBM_PEAK_GBPS:.1f}% |")
         out.append(f"<!-- {wl} decode_avg_us: {avg:.3f} -->")
-    if gathers:
-        out += ["", "Gather probe launches (median us by grid size): " +
-                ", ".join(f"{g // 64} waves: {u:.2f}" for g, u in sorted(gathers.items()))]
+    if workload is not None and gathers:
+        cfg = di.CONFIGS[workload]
+        lay = di.make_layout(cfg)
+        kvb = kv_read_bytes(cfg, lay.context_lens)
+        sig, grid = keys[workload]
+        dec = [d for (n, g), ds in groups.items() for d in ds
+               if g == grid and n == "paged_decode_kernel<%s, %s, %d, %d>" % sig]
+        best_g = min(gathers.values())
+        streams = {g: statistics.median(v) for (n, g), v in groups.items()
+                   if n.startswith("stream_read")}
+        out += ["", f"Bandwidth probes of this run ({workload}: {kvb} bytes of valid K/V rows per "
+                "call), median us by wavefront count:", "",
+                "| probe | " + " | ".join(f"{g // 64} waves" for g in sorted(gathers)) + " |",
+                "|---|" + "---|" * len(gathers),
+                "| gather (same tables) | " + " | ".join(f"{gathers[g]:.2f}" for g in sorted(gathers)) + " |"]
+        if streams:
+            out.append("| stream read (same bytes) | " +
+                       " | ".join(f"{streams.get(g, float('nan')):.2f}" for g in sorted(gathers)) + " |")
+        if dec:
+            avg = statistics.fmean(dec)
+            out += ["", f"Fastest gather: {best_g:.2f} us = {kvb / (best_g * 1e-6) / 1e9:.1f} GB/s "
+                    f"({100 * kvb / (best_g * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}% of 8 TB/s). "
+                    f"Decode average {avg:.2f} us: {100 * best_g / avg:.1f}% of the gather's rate.",
+                    f"<!-- {workload} gather_best_us: {best_g:.3f} -->"]
     out += ["", f"kernel_source_sha256: {kernel_source_sha256()}"]
     return "\n".join(out) + "\n"
 
@@ -946,8 +974,10 @@ def main(argv=None) -> int:
         if kind not in ("trace", "pmc"):
             print("--summarize KIND must be 'trace' or 'pmc'", file=sys.stderr)
             return 2
-        fn = summarize_trace if kind == "trace" else summarize_pmc
-        sys.stdout.write(fn(root, args.summary_command))
+        if kind == "trace":
+            sys.stdout.write(summarize_trace(root, args.summary_command, args.summary_workload))
+        else:
+            sys.stdout.write(summarize_pmc(root, args.summary_command))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -95,3 +95,12 @@ def test_decode_kernel_names_parse_in_both_forms():
     assert bench.decode_kernel_sig("void photon::(anonymous namespace)::paged_decode_kernel<float, float, 64, 4>(photon::(anonymous namespace)::KernelArgs)") \
         == ("float", "float", 64, 4)
     assert bench.decode_kernel_sig("paged_mq_kernel<float, float, 64, 4>") is None
+
+
+def test_kernel_names_in_summaries():
+    import bench
+    assert bench.short_kernel_name("void photon::rope_kv_cache_write_kernel<float, 64, false>(x)") \
+        == "rope_kv_cache_write_kernel<float, 64, false>"
+    assert bench.short_kernel_name("photon::kv_cache_write_kernel(x)") == "kv_cache_write_kernel"
+    assert bench.short_kernel_name("_ZN6photon12_GLOBAL__N_113gather_kernelILi256EEEvNS0_10GatherArgsE") \
+        == "gather_kernel<256>"
