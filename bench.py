@@ -818,8 +818,9 @@ def summarize_trace(root: str, command: str, workload: str | None = None) -> str
         dur = (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3
         groups.setdefault((short_kernel_name(name), grid), []).append(dur)
     total = sum(sum(v) for v in groups.values())
-    out = ["# Kernel durations (rocprofv3 kernel trace): decode on every workload, the bandwidth "
-           "probes and the other kernels the benchmark runs", "",
+    title = (f"the {workload} workload: its decode kernel, its bandwidth probes and the other "
+             "kernels of the run") if workload else "every kernel of the run"
+    out = [f"# Kernel durations (rocprofv3 kernel trace), {title}", "",
            "Command ($REPO is the repository root):", "",
            "```", command, "```", "",
            "| kernel | grid (threads) | calls | average (us) | median (us) | min (us) | max (us) | share |",
