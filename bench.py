@@ -773,15 +773,18 @@ def workload_dispatch_keys(names) -> dict:
 def planned_waves(desc) -> int:
     """Wavefronts the library launches for ``desc`` with automatic
     partitioning: one per unit of the largest batch the descriptor allows,
-    but no more than 256 compute units x max(4, 64 KiB / unit bytes), in
-    whole workgroups of four (the rule include/photon_decode.h states for
-    partition_tokens = 0; a CPU test checks it against the workspace size)."""
+    but no more than 256 compute units x max(4, 64 KiB / bytes in flight per
+    wave), in whole workgroups of four (the rule include/photon_decode.h
+    states for partition_tokens = 0; a CPU test checks it against the
+    workspace size).  A wave keeps two chunks in flight, one with eight
+    query heads per KV head."""
     import paged_attention_decode_photon_amd as pa
     quantum = pa.partition_quantum(desc)
     eb = 4 if desc.kv.dtype == pa.F32 else 2
     chunks = -(-desc.max_context_len // quantum)
     upper = desc.num_seqs * desc.kv.num_kv_heads * chunks
-    per_cu = max(4, (64 * 1024) // (2 * quantum * desc.kv.head_dim * eb))
+    in_flight = 2 if desc.num_q_heads // desc.kv.num_kv_heads < 8 else 1
+    per_cu = max(4, (64 * 1024) // (2 * quantum * desc.kv.head_dim * eb * in_flight))
     waves = max(1, min(upper, 256 * per_cu))
     return -(-waves // 4) * 4
 

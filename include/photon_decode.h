@@ -109,7 +109,10 @@ typedef struct photon_decode_desc {
                                    <= max_blocks_per_seq * block_size; sizes the
                                    grid and the workspace                        */
     int32_t partition_tokens;   /* 0 = automatic (enough wavefronts for about
-                                   64 KiB of K/V reads in flight per CU);
+                                   64 KiB of K/V reads in flight per CU,
+                                   counting the two chunks a wavefront keeps
+                                   in flight, one with eight query heads per
+                                   KV head; at least one per SIMD);
                                    otherwise the most tokens one wavefront
                                    handles when every sequence is at
                                    max_context_len, a positive multiple of

@@ -37,6 +37,11 @@ constexpr int decode_chunk_blocks(int elem_bytes, int head_dim, int group)
                                                                                            : 1;
 }
 
+// Chunks a decode wavefront keeps in flight: two register sets alternate
+// (the next chunk loads while the current one is used), except with eight
+// query heads per KV head, where a second set would cost occupancy.
+constexpr int decode_chunks_in_flight(int group) { return group < 8 ? 2 : 1; }
+
 // Tokens one decode wavefront handles per loop step (the partition quantum).
 constexpr int decode_chunk_tokens(int elem_bytes, int head_dim, int group)
 {

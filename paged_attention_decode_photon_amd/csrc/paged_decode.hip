@@ -467,7 +467,7 @@ struct WaveDecoder {
     // automatic plan launches for 16-bit storage; those go one at a time.
     __device__ void run_chunks(int ch0, int ch1)
     {
-        if constexpr (G < 8) {
+        if constexpr (decode_chunks_in_flight(G) == 2) {
             u32x4 ka[NU], va[NU], kb[NU], vb[NU];
             issue_chunk(ch0, ka, va);
             for (int ch = ch0;;) {

@@ -82,9 +82,13 @@ static_assert(PHOTON_F32 == photon::kDtypeF32 && PHOTON_F16 == photon::kDtypeF16
 constexpr int32_t kKnownDecodeFlags = PHOTON_DECODE_OUT_F32;
 
 // Default number of decode wavefronts: enough per compute unit of an MI355X
-// (256 CUs) that the units being read, one per wave, add up to 64 KiB in
-// flight per CU, and at least four.  Each wave takes an equal share of the
-// batch's units.
+// (256 CUs) that the chunks in flight, counting every chunk a wave keeps in
+// flight, add up to 64 KiB per CU, and at least four (one per SIMD).  Each
+// wave takes an equal share of the batch's units.  Counting one chunk per
+// wave instead put two waves on every SIMD for 16-bit rows with two chunks
+// in flight; one per SIMD is faster there (ragged f16 batch of 64:
+// 27.1 -> 25.6 us), while with one chunk in flight (eight query heads per
+// KV head) two per SIMD stay faster (32.2 against 34.6 us).
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kBytesInFlightPerCu = 64 * 1024;
 constexpr int64_t kMinWavesPerCu = 4;
@@ -174,7 +178,7 @@ photon_status plan_decode(const photon_decode_desc *d, Plan *plan)
         waves = (upper + per_wave - 1) / per_wave;
     } else {
         const int64_t unit_bytes = 2LL * p.quantum * d->kv.head_dim * p.elem_bytes;  // K + V
-        int64_t per_cu = kBytesInFlightPerCu / unit_bytes;
+        int64_t per_cu = kBytesInFlightPerCu / (unit_bytes * photon::decode_chunks_in_flight(group));
         per_cu = per_cu < kMinWavesPerCu ? kMinWavesPerCu : per_cu;
         const int64_t auto_waves = kComputeUnits * per_cu;
         waves = upper < auto_waves ? upper : auto_waves;
