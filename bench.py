@@ -595,30 +595,52 @@ def time_graph(calls, stream, steps: int, warmup: int) -> dict:
 
 
 PROBE_WAVES = (1024, 2048, 4096, 8192)
+# LDS-staged gather settings: (workgroups of four wavefronts, tiles in flight
+# per wavefront); those whose ring does not fit the row size are skipped.
+STAGED_PROBES = ((256, 2), (256, 4), (512, 2), (512, 4), (1024, 2))
+# queue-driven gather: wavefronts, thousandths split statically, tiles per piece
+QUEUE_PROBE = (1024, 900, 4)
 
 
 def gather_ceiling(pools, tables, lens, max_ctx: int, kv_bytes: int, stream, steps, warmup) -> dict:
     """Bare gather of the decode call's K/V rows through its tables (no
     arithmetic), over every (k_cache, v_cache) pair in ``pools``, one call
-    each per replay; the fastest wavefront count is the ceiling."""
+    each per replay: from register sets at several wavefront counts and
+    from LDS rings at several workgroup counts and depths; the fastest is the
+    ceiling.  Also times one queue-driven setting (part of the work handed
+    out at run time), which is not a ceiling candidate."""
     import paged_attention_decode_photon_amd as pa
     import torch
     lib = pa.get_lib()
-    sink = torch.empty(max(PROBE_WAVES), dtype=torch.int32, device=tables.device)
+    sink = torch.empty(max(max(PROBE_WAVES), 4 * max(w for w, _ in STAGED_PROBES)),
+                       dtype=torch.int32, device=tables.device)
+    queue = torch.zeros(1, dtype=torch.int64, device=tables.device)
     desc = pa.DecodeDesc(lens.shape[0], pools[0][0].shape[1], tables.shape[1], max_ctx, 0,
                          pa.kv_desc(pools[0][0]), 0)
     dref = ctypes.byref(desc)
-    by_waves = {}
-    for waves in PROBE_WAVES:
-        calls = [functools.partial(_checked, lib.photon_probe_gather, kc.data_ptr(), vc.data_ptr(),
-                                   tables.data_ptr(), lens.data_ptr(), dref, waves,
-                                   sink.data_ptr()) for kc, vc in pools]
-        by_waves[waves] = time_graph(calls, stream, steps, warmup)["us_median"]
-    best = min(by_waves, key=by_waves.get)
-    us = by_waves[best]
-    return {"kernel": "gather_kernel (photon_probe_gather)", "bytes_per_call": kv_bytes,
-            "us_per_call_by_waves": {str(k): v for k, v in by_waves.items()}, "best_waves": best,
-            "us_per_call": us, "gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+    row_bytes = pools[0][0].shape[3] * pools[0][0].element_size()
+
+    def timed(fn, *args):
+        calls = [functools.partial(_checked, fn, kc.data_ptr(), vc.data_ptr(), tables.data_ptr(),
+                                   lens.data_ptr(), dref, *args) for kc, vc in pools]
+        return time_graph(calls, stream, steps, warmup)["us_median"]
+
+    by_waves = {w: timed(lib.photon_probe_gather, w, sink.data_ptr()) for w in PROBE_WAVES}
+    staged = {f"{w}x{r}": timed(lib.photon_probe_gather_staged, w, r, sink.data_ptr())
+              for w, r in STAGED_PROBES if r * row_bytes <= 1024}
+    qw, qs, qp = QUEUE_PROBE
+    queued = timed(lib.photon_probe_gather_queue, qw, qs, qp, queue.data_ptr(), sink.data_ptr())
+    cands = {f"register sets, {w} waves": v for w, v in by_waves.items()}
+    cands.update({f"LDS ring, {k.replace('x', ' workgroups x ')} tiles": v for k, v in staged.items()})
+    best = min(cands, key=cands.get)
+    us = cands[best]
+    return {"kernel": "gather_kernel / gather_staged_kernel (photon_probe_gather, "
+                      "photon_probe_gather_staged)",
+            "bytes_per_call": kv_bytes,
+            "us_per_call_by_waves": {str(k): v for k, v in by_waves.items()},
+            "staged_us_by_workgroups_x_ring": staged,
+            "queue_us": {f"{qw} waves, {qs}/1000 static, {qp}-tile pieces": queued},
+            "best": best, "us_per_call": us, "gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
@@ -744,11 +766,18 @@ def short_kernel_name(name: str) -> str:
     if sig:
         return "paged_decode_kernel<%s, %s, %d, %d>" % sig
     # longer names first: "rope_kv_cache_write_kernel" contains "kv_cache_write_kernel"
-    for key in ("gather_kernel", "stream_read_kernel", "paged_mq_wide_kernel", "paged_mq_kernel",
+    for key in ("gather_staged_kernel", "gather_queue_kernel", "gather_kernel",
+                "stream_read_kernel", "paged_mq_wide_kernel", "paged_mq_kernel",
                 "rope_kv_cache_write_kernel", "kv_cache_write_kernel", "__amd_rocclr_copyBuffer"):
         if key in name:
-            m = re.search(key + r"<([^>]*)>", name) or re.search(key + r"ILi(\d+)E", name)
-            return f"{key}<{m.group(1)}>" if m else key
+            m = re.search(key + r"<([^>]*)>", name)
+            if m:
+                return f"{key}<{m.group(1)}>"
+            m = re.search(key + r"I((?:Li\d+E)+)E", name)  # mangled integer template arguments
+            if m:
+                args = re.findall(r"Li(\d+)E", m.group(1))
+                return key + "<" + ", ".join(args) + ">"
+            return key
     return name[:60]
 
 
@@ -806,6 +835,26 @@ def _col(row: dict, *names):
     raise KeyError(names)
 
 
+def probe_rows(groups: dict) -> list:
+    """(design, setting, median us, ceiling candidate) of every probe kernel
+    in a trace's (kernel, grid threads) -> durations groups."""
+    rows = []
+    for (name, grid), v in sorted(groups.items()):
+        med = statistics.median(v)
+        if name.startswith("gather_kernel"):
+            rows.append(("gather, register sets", f"{grid // 64} waves", med, True))
+        elif name.startswith("gather_staged_kernel"):
+            ring = name.split(",")[-1].strip(" >")
+            rows.append(("gather, LDS ring", f"{grid // 256} workgroups x {ring} tiles", med, True))
+        elif name.startswith("gather_queue_kernel"):
+            w, st, pc = QUEUE_PROBE
+            rows.append(("gather, queue-driven", f"{grid // 64} waves, {st}/1000 static, "
+                         f"{pc}-tile pieces", med, False))
+        elif name.startswith("stream_read"):
+            rows.append(("stream read", f"{grid // 64} waves", med, False))
+    return rows
+
+
 def summarize_trace(root: str, command: str, workload: str | None = None) -> str:
     """Markdown summary of a rocprofv3 --kernel-trace run: per-kernel
     durations, the decode kernel split by workload (signature and grid) with
@@ -834,9 +883,6 @@ def summarize_trace(root: str, command: str, workload: str | None = None) -> str
                    f"{100 * sum(v) / total:.1f}% |")
     out.append("")
     keys = workload_dispatch_keys(list(di.CONFIGS))
-    gathers = {g: statistics.median(v) for (n, g), v in groups.items() if n.startswith("gather")}
-    if workload is None:
-        gathers = {}  # several workloads' probes share kernels and grids
     out += ["Decode kernel by workload (fused append + decode launches; algorithmic bytes as in "
             "`bench.decode_bytes` plus the new rows read and appended):", "",
             "| workload | launches | average (us) | median (us) | bytes per launch | GB/s at the average "
@@ -855,30 +901,30 @@ def summarize_trace(root: str, command: str, workload: str | None = None) -> str
         out.append(f"| {wl} | {len(v)} | {avg:.2f} | {statistics.median(v):.2f} | {nbytes} | "
                    f"{gbps:.1f} | {100 * gbps / HBM_PEAK_GBPS:.1f}% |")
         out.append(f"<!-- {wl} decode_avg_us: {avg:.3f} -->")
-    if workload is not None and gathers:
+    # several workloads' probes share kernels and grids: probes only for a one-workload run
+    probes = probe_rows(groups) if workload is not None else []
+    ceiling = [p for p in probes if p[3]]
+    if ceiling:
         cfg = di.CONFIGS[workload]
         lay = di.make_layout(cfg)
         kvb = kv_read_bytes(cfg, lay.context_lens)
         sig, grid = keys[workload]
         dec = [d for (n, g), ds in groups.items() for d in ds
                if g == grid and n == "paged_decode_kernel<%s, %s, %d, %d>" % sig]
-        best_g = min(gathers.values())
-        streams = {g: statistics.median(v) for (n, g), v in groups.items()
-                   if n.startswith("stream_read")}
+        best = min(ceiling, key=lambda p: p[2])
         out += ["", f"Bandwidth probes of this run ({workload}: {kvb} bytes of valid K/V rows per "
-                "call), median us by wavefront count:", "",
-                "| probe | " + " | ".join(f"{g // 64} waves" for g in sorted(gathers)) + " |",
-                "|---|" + "---|" * len(gathers),
-                "| gather (same tables) | " + " | ".join(f"{gathers[g]:.2f}" for g in sorted(gathers)) + " |"]
-        if streams:
-            out.append("| stream read (same bytes) | " +
-                       " | ".join(f"{streams.get(g, float('nan')):.2f}" for g in sorted(gathers)) + " |")
+                "call; the gathers read exactly those rows through the same tables, the stream "
+                "read as many contiguous bytes), median us:", "",
+                "| probe | setting | median (us) | GB/s |", "|---|---|---|---|"]
+        for design, setting, med, _ in probes:
+            out.append(f"| {design} | {setting} | {med:.2f} | {kvb / (med * 1e-6) / 1e9:.1f} |")
         if dec:
             avg = statistics.fmean(dec)
-            out += ["", f"Fastest gather: {best_g:.2f} us = {kvb / (best_g * 1e-6) / 1e9:.1f} GB/s "
-                    f"({100 * kvb / (best_g * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}% of 8 TB/s). "
-                    f"Decode average {avg:.2f} us: {100 * best_g / avg:.1f}% of the gather's rate.",
-                    f"<!-- {workload} gather_best_us: {best_g:.3f} -->"]
+            out += ["", f"Fastest gather: {best[0]}, {best[1]}: {best[2]:.2f} us = "
+                    f"{kvb / (best[2] * 1e-6) / 1e9:.1f} GB/s "
+                    f"({100 * kvb / (best[2] * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}% of 8 TB/s). "
+                    f"Decode average {avg:.2f} us: {100 * best[2] / avg:.1f}% of the gather's rate.",
+                    f"<!-- {workload} gather_best_us: {best[2]:.3f} -->"]
     out += ["", f"kernel_source_sha256: {kernel_source_sha256()}"]
     return "\n".join(out) + "\n"
 

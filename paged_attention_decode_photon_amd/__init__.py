@@ -129,6 +129,12 @@ def _load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.photon_probe_stream_read.restype = st
     lib.photon_probe_gather.argtypes = [vp, vp, vp, vp, ctypes.POINTER(DecodeDesc), i32, vp, vp]
     lib.photon_probe_gather.restype = st
+    lib.photon_probe_gather_staged.argtypes = [vp, vp, vp, vp, ctypes.POINTER(DecodeDesc), i32, i32,
+                                               vp, vp]
+    lib.photon_probe_gather_staged.restype = st
+    lib.photon_probe_gather_queue.argtypes = [vp, vp, vp, vp, ctypes.POINTER(DecodeDesc), i32, i32,
+                                              i32, vp, vp, vp]
+    lib.photon_probe_gather_queue.restype = st
     lib.photon_status_str.argtypes = [st]
     lib.photon_status_str.restype = ctypes.c_char_p
     lib.photon_last_error_detail.argtypes = []
@@ -509,22 +515,63 @@ def probe_stream_read(buf, waves: int, sink=None):
     return sink
 
 
+def _gather_desc(k_cache, v_cache, block_tables, context_lens, max_context_len: int):
+    _int32(block_tables=block_tables, context_lens=context_lens)
+    _args_ok(k_cache.device, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+             context_lens=context_lens)
+    return DecodeDesc(context_lens.shape[0], k_cache.shape[1], block_tables.shape[1],
+                      int(max_context_len), 0, kv_desc(k_cache), 0)
+
+
 def probe_gather(k_cache, v_cache, block_tables, context_lens, max_context_len: int, waves: int,
                  sink=None):
     """Bandwidth probe: read every valid K and V row of the decode call over
     these tables and lengths, split evenly over ``waves`` wavefronts, no
     arithmetic.  Returns the per-wavefront XORs (include/photon_probe.h)."""
     import torch
-    _int32(block_tables=block_tables, context_lens=context_lens)
-    _args_ok(k_cache.device, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
-             context_lens=context_lens)
-    hkv = k_cache.shape[1]
-    desc = DecodeDesc(context_lens.shape[0], hkv, block_tables.shape[1], int(max_context_len), 0,
-                      kv_desc(k_cache), 0)
+    desc = _gather_desc(k_cache, v_cache, block_tables, context_lens, max_context_len)
     if sink is None:
         sink = torch.empty(waves, dtype=torch.int32, device=k_cache.device)
     check(get_lib().photon_probe_gather(k_cache.data_ptr(), v_cache.data_ptr(),
                                         block_tables.data_ptr(), context_lens.data_ptr(),
                                         ctypes.byref(desc), int(waves), sink.data_ptr(),
                                         _stream_ptr(k_cache)))
+    return sink
+
+
+def probe_gather_staged(k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                        workgroups: int, ring_tiles: int, sink=None):
+    """The rows of ``probe_gather`` over ``workgroups`` workgroups of four
+    wavefronts, each wavefront keeping ``ring_tiles`` tiles in flight in
+    LDS.  Returns the per-wavefront XORs (4 per workgroup)."""
+    import torch
+    desc = _gather_desc(k_cache, v_cache, block_tables, context_lens, max_context_len)
+    if sink is None:
+        sink = torch.empty(4 * workgroups, dtype=torch.int32, device=k_cache.device)
+    check(get_lib().photon_probe_gather_staged(k_cache.data_ptr(), v_cache.data_ptr(),
+                                               block_tables.data_ptr(), context_lens.data_ptr(),
+                                               ctypes.byref(desc), int(workgroups),
+                                               int(ring_tiles), sink.data_ptr(),
+                                               _stream_ptr(k_cache)))
+    return sink
+
+
+def probe_gather_queue(k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                       waves: int, static_permille: int, piece_tiles: int, queue, sink=None):
+    """The rows of ``probe_gather``, the last (1000 - static_permille)
+    thousandths handed out at run time in pieces of ``piece_tiles`` tiles
+    through ``queue`` (one int64 on the device, zero before the call and
+    zero again after it).  Returns the per-wavefront XORs."""
+    import torch
+    desc = _gather_desc(k_cache, v_cache, block_tables, context_lens, max_context_len)
+    _args_ok(k_cache.device, queue=queue)
+    if queue.dtype != torch.int64 or queue.numel() < 1:
+        raise PhotonError(ERR_INVALID_ARG, "PHOTON_ERR_INVALID_ARG", "queue must hold one int64")
+    if sink is None:
+        sink = torch.empty(waves, dtype=torch.int32, device=k_cache.device)
+    check(get_lib().photon_probe_gather_queue(k_cache.data_ptr(), v_cache.data_ptr(),
+                                              block_tables.data_ptr(), context_lens.data_ptr(),
+                                              ctypes.byref(desc), int(waves), int(static_permille),
+                                              int(piece_tiles), queue.data_ptr(), sink.data_ptr(),
+                                              _stream_ptr(k_cache)))
     return sink

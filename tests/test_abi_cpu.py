@@ -429,3 +429,29 @@ def test_probes_validate_before_any_hip_call():
     assert gather(dd(maxctx=128 * 16 + 1)) == pa.ERR_INVALID_ARG
     assert gather(dd(), kc=None) == pa.ERR_INVALID_ARG
     assert gather(dd(), waves=3) == pa.ERR_INVALID_ARG
+
+    def staged(desc, wgs=256, ring=2, kc=FAKE, sink=FAKE):
+        return lib.photon_probe_gather_staged(kc, FAKE, FAKE, FAKE, ctypes.byref(desc), wgs, ring,
+                                              sink, None)
+
+    assert staged(dd(), wgs=0) == pa.ERR_INVALID_ARG
+    assert staged(dd(), wgs=(1 << 18) + 1) == pa.ERR_INVALID_ARG
+    assert staged(dd(), ring=3) == pa.ERR_UNSUPPORTED
+    assert staged(dd(), ring=8) == pa.ERR_UNSUPPORTED    # 256-byte rows: 4 tiles fill 128 KiB
+    assert staged(dd(d=128), ring=4) == pa.ERR_UNSUPPORTED
+    assert staged(dd(b=65)) == pa.ERR_UNSUPPORTED
+    assert staged(dd(), kc=None) == pa.ERR_INVALID_ARG
+    assert staged(dd(), sink=None) == pa.ERR_INVALID_ARG
+
+    def queue(desc, waves=64, permille=500, piece=4, q=FAKE):
+        return lib.photon_probe_gather_queue(FAKE, FAKE, FAKE, FAKE, ctypes.byref(desc), waves,
+                                             permille, piece, q, FAKE, None)
+
+    assert queue(dd(), waves=6) == pa.ERR_INVALID_ARG
+    assert queue(dd(), permille=-1) == pa.ERR_INVALID_ARG
+    assert queue(dd(), permille=1001) == pa.ERR_INVALID_ARG
+    assert queue(dd(), piece=0) == pa.ERR_INVALID_ARG
+    assert queue(dd(), piece=65) == pa.ERR_INVALID_ARG
+    assert queue(dd(), q=None) == pa.ERR_INVALID_ARG
+    assert queue(dd(), q=FAKE + 4) == pa.ERR_INVALID_ARG
+    assert queue(dd(b=65)) == pa.ERR_UNSUPPORTED

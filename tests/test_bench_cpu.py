@@ -104,3 +104,24 @@ def test_kernel_names_in_summaries():
     assert bench.short_kernel_name("photon::kv_cache_write_kernel(x)") == "kv_cache_write_kernel"
     assert bench.short_kernel_name("_ZN6photon12_GLOBAL__N_113gather_kernelILi256EEEvNS0_10GatherArgsE") \
         == "gather_kernel<256>"
+
+
+def test_probe_kernels_in_summaries():
+    import bench
+    assert bench.short_kernel_name(
+        "_ZN6photon12_GLOBAL__N_120gather_staged_kernelILi256ELi2EEEvNS0_10GatherArgsEi") \
+        == "gather_staged_kernel<256, 2>"
+    assert bench.short_kernel_name(
+        "void photon::(anonymous namespace)::gather_staged_kernel<128, 8>(x, int)") \
+        == "gather_staged_kernel<128, 8>"
+    assert bench.short_kernel_name(
+        "_ZN6photon12_GLOBAL__N_119gather_queue_kernelILi512EEEvNS0_10GatherArgsEPyii") \
+        == "gather_queue_kernel<512>"
+    groups = {("gather_kernel<256>", 65536): [15.4, 15.6], ("gather_staged_kernel<256, 4>", 65536): [15.1],
+              ("gather_queue_kernel<256>", 65536): [27.0], ("stream_read_kernel", 262144): [13.0],
+              ("paged_mq_kernel<float, float, 64, 4>", 256): [25.0]}
+    rows = {(d, s): (m, c) for d, s, m, c in bench.probe_rows(groups)}
+    assert rows == {("gather, register sets", "1024 waves"): (15.5, True),
+                    ("gather, LDS ring", "256 workgroups x 4 tiles"): (15.1, True),
+                    ("gather, queue-driven", "1024 waves, 900/1000 static, 4-tile pieces"): (27.0, False),
+                    ("stream read", "4096 waves"): (13.0, False)}

@@ -1,7 +1,7 @@
 """The bandwidth probes read exactly the bytes they claim to read: the XOR of
 their per-wavefront checksums equals the XOR of every 32-bit word of the
 buffer (streaming read) or of every valid K and V row of the decode call
-(gather), computed here with numpy."""
+(the three gathers), computed here with numpy."""
 import numpy as np
 import pytest
 import torch
@@ -92,3 +92,70 @@ def test_gather_head_dim_128(pa):
         got = sink_xor(sink)
         want = valid_rows_xor(kc.view(bits), vc.view(bits), tables, ctx)
         assert got == want, f"{np.dtype(dtype)}: {got:#x} != {want:#x}"
+
+
+def gather_case(name):
+    cfg = di.CONFIGS[name]
+    lay = di.make_layout(cfg)
+    t = di.make_layer(cfg, lay)
+    kc = di.poison_unused(cfg, lay, t.k_cache)
+    vc = di.poison_unused(cfg, lay, t.v_cache)
+    dev = [di.to_torch(x).to("cuda:0") for x in (kc, vc, lay.block_tables, lay.context_lens)]
+    want = valid_rows_xor(di.storage_bits(kc), di.storage_bits(vc), lay.block_tables,
+                          lay.context_lens)
+    return dev, lay.max_context_len, want
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b_b1", "llama1b_b16", "cb_b64", "llama1b_b16_bf16"])
+def test_staged_gather_checksum(pa, name):
+    (kc, vc, tables, lens), max_ctx, want = gather_case(name)
+    rings = (2, 4, 8) if di.CONFIGS[name].elem_bytes == 2 else (2, 4)
+    for wgs in (1, 7, 256, 1024):
+        for ring in rings:
+            sink = pa.probe_gather_staged(kc, vc, tables, lens, max_ctx, wgs, ring)
+            torch.cuda.synchronize()
+            got = sink_xor(sink)
+            assert got == want, f"{name}, {wgs} workgroups, ring {ring}: {got:#x} != {want:#x}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b_b1", "llama1b_b16", "cb_b64", "llama1b_b16_bf16"])
+def test_queue_gather_checksum(pa, name):
+    (kc, vc, tables, lens), max_ctx, want = gather_case(name)
+    queue = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    for waves in (4, 1024):
+        for permille, piece in ((0, 1), (500, 4), (900, 16), (1000, 8), (0, 64)):
+            for rep in range(2):  # the second call relies on the first leaving zero behind
+                sink = pa.probe_gather_queue(kc, vc, tables, lens, max_ctx, waves, permille, piece,
+                                             queue)
+                torch.cuda.synchronize()
+                got = sink_xor(sink)
+                assert got == want, \
+                    f"{name}, {waves} waves, {permille} static, pieces of {piece}, call {rep}: " \
+                    f"{got:#x} != {want:#x}"
+                assert int(queue.item()) == 0
+
+
+def test_staged_and_queue_gathers_head_dim_128(pa):
+    rng = np.random.default_rng(6)
+    ctx = np.array([0, 1, 17, 300, 33], np.int32)
+    need = (ctx + 15) // 16
+    nb = int(need.sum()) + 2
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((5, int(need.max())), -1, np.int32)
+    p = 0
+    for i, n in enumerate(need):
+        tables[i, :n] = perm[p:p + n]
+        p += n
+    for dtype, ring in ((np.float32, 2), (np.float16, 4)):
+        kc = rng.standard_normal((nb, 3, 16, 128)).astype(dtype)
+        vc = rng.standard_normal((nb, 3, 16, 128)).astype(dtype)
+        bits = np.uint32 if dtype == np.float32 else np.uint16
+        want = valid_rows_xor(kc.view(bits), vc.view(bits), tables, ctx)
+        args = (torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(),
+                torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(), 300)
+        got = sink_xor(pa.probe_gather_staged(*args, 3, ring))
+        assert got == want, f"{np.dtype(dtype)} staged: {got:#x} != {want:#x}"
+        queue = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+        got = sink_xor(pa.probe_gather_queue(*args, 64, 250, 2, queue))
+        assert got == want, f"{np.dtype(dtype)} queue: {got:#x} != {want:#x}"
+        assert int(queue.item()) == 0
