@@ -12,7 +12,8 @@
 //
 // Claim.  Before counting, a producer swaps the word from 0 to (epoch, 0)
 // with a compare-and-swap, issued together with its partial-record stores so
-// that the wait for those stores also covers it.  If the swap returns a
+// that the wait for those stores also covers it (or earlier, where the
+// decode kernel measured that faster).  If the swap returns a
 // stale value, a second swap replaces exactly that value; when it fails,
 // another producer of this call has claimed the word already.  Every
 // producer claims before it counts, and the claim precedes its count in the
