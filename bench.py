@@ -1260,6 +1260,9 @@ def main(argv=None) -> int:
         "decode_call_us_single_event_pair": round(single_us, 3),
         "decode_gbps_event_timed": round(achieved, 2),
         "copy_gbps_read_plus_write": round(copy_gbps, 1) if copy_gbps else None,
+        # the step's algorithmic rate against that copy's (reads plus writes
+        # of a >= 1 GiB device copy, the achievable-bandwidth reference)
+        "pct_of_copy_bandwidth": round(100 * value / copy_gbps, 2) if copy_gbps else None,
         "kernel_source_sha256": kernel_source_sha256(),
         "roofline": {
             "bound": "hbm",
