@@ -312,7 +312,9 @@ PHOTON_API photon_status photon_paged_attn_workspace_bytes(const photon_decode_d
  * evenly over its wavefronts, whatever the mix of context lengths; a
  * (sequence, KV head) split over several wavefronts is merged by the last of
  * them to finish, in a fixed order, so results are deterministic run to run.
- * num_seqs is at most 2048 (PHOTON_ERR_UNSUPPORTED above).
+ * num_seqs is at most 2048, and num_seqs * num_kv_heads * (units of
+ * max_context_len + 2) at most INT32_MAX, where a unit is the kernel's
+ * 16- or 32-token chunk (PHOTON_ERR_UNSUPPORTED above either).
  *
  *   q             [num_seqs, num_q_heads, head_dim]        kv.dtype, 16-byte aligned
  *   k_cache, v_cache  pools (read only), 16-byte aligned

@@ -8,6 +8,7 @@
 namespace photon {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
@@ -59,6 +60,13 @@ struct Elem<_Float16> {
         return v;
     }
     __device__ static _Float16 from_float(float x) { return (_Float16)x; }
+    __device__ static uint32_t pack2(float lo, float hi)
+    {
+        half2_t h;
+        h[0] = (_Float16)lo;
+        h[1] = (_Float16)hi;
+        return __builtin_bit_cast(uint32_t, h);
+    }
     // acc + x.lo * y.lo + x.hi * y.hi over two packed elements, in fp32
     // (v_dot2_f32_f16; the products of two halves are exact in fp32).
     __device__ static float dot2(uint32_t x, uint32_t y, float acc)
@@ -95,6 +103,13 @@ struct Elem<__bf16> {
         return v;
     }
     __device__ static __bf16 from_float(float x) { return (__bf16)x; }
+    __device__ static uint32_t pack2(float lo, float hi)
+    {
+        bf162_t h;
+        h[0] = (__bf16)lo;
+        h[1] = (__bf16)hi;
+        return __builtin_bit_cast(uint32_t, h);
+    }
     // acc + x.lo * y.lo + x.hi * y.hi in fp32 (v_dot2_f32_bf16).
     __device__ static float dot2(uint32_t x, uint32_t y, float acc)
     {
@@ -103,19 +118,32 @@ struct Elem<__bf16> {
     }
 };
 
-// Store E consecutive outputs of type O (E * sizeof(O) is 16 or 32 bytes).
-template <typename O, int E>
-__device__ __forceinline__ void store_out(O *dst, const float (&v)[E])
+// Store N consecutive outputs of type O (N a power of two up to 8; dst
+// aligned to N * sizeof(O) bytes, at most 16).
+template <typename O, int N>
+__device__ __forceinline__ void store_out_n(O *dst, const float (&v)[N])
 {
     if constexpr (sizeof(O) == 4) {
+        if constexpr (N >= 4) {
 #pragma unroll
-        for (int k = 0; k < E / 4; ++k)
-            *reinterpret_cast<u32x4 *>(dst + 4 * k) =
-                u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
-                      __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
-    } else {
-        static_assert(E * sizeof(O) == 16, "one 16-byte store");
+            for (int k = 0; k < N / 4; ++k)
+                *reinterpret_cast<u32x4 *>(dst + 4 * k) =
+                    u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                          __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
+        } else if constexpr (N == 2) {
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{__float_as_uint(v[0]), __float_as_uint(v[1])};
+        } else {
+            *dst = v[0];
+        }
+    } else if constexpr (N == 8) {
         *reinterpret_cast<u32x4 *>(dst) = Elem<O>::pack(v);
+    } else if constexpr (N == 4) {
+        *reinterpret_cast<u32x2 *>(dst) =
+            u32x2{Elem<O>::pack2(v[0], v[1]), Elem<O>::pack2(v[2], v[3])};
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<uint32_t *>(dst) = Elem<O>::pack2(v[0], v[1]);
+    } else {
+        *dst = Elem<O>::from_float(v[0]);
     }
 }
 

@@ -67,6 +67,11 @@ constexpr int kWideTiles = PHOTON_MQ_WIDE_TILES;
 // Sequences per call: the decode kernel keeps per-sequence prefix sums in LDS.
 constexpr int kMaxDecodeSeqs = 2048;
 
+// Empty units charged at the start of each non-empty segment in the decode
+// kernel's split of larger calls (the kernel explains the choice).  The
+// charged list of units is indexed with 32-bit integers.
+constexpr int kDecodeBoundaryUnits = 2;
+
 struct DecodeArgs {
     const void *q;
     const void *k_cache;

@@ -103,7 +103,7 @@ constexpr int kMinWaves = 256;
 // best among one to three (ragged batch-64: 29.6 -> 28.2 us).  From
 // 3 * kMinWaves units on, every slice holds at least three list entries, so
 // at least one unit of work (batch 4: 14.8 -> 13.6 us at fp32).
-constexpr int kBoundaryUnits = 2;
+constexpr int kBoundaryUnits = kDecodeBoundaryUnits;
 constexpr int kChargeFromUnits = 3 * kMinWaves;
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
@@ -192,16 +192,28 @@ struct KernelArgs {
     uint32_t epoch;  // this call's number, never 0
 };
 
+// floor(n / d) for wave-uniform integers 0 <= n < 2^53 and 0 < d < 2^31,
+// held exactly in doubles.  A 64-bit integer division compiles to several
+// hundred scalar instructions (about 0.2 us of a wave's time, on the path
+// of every slice's start and every merge); this is a dozen vector ones.
+// Exact: when n / d is not an integer it lies at least 1 / d below the next
+// one, while the correctly rounded quotient is off by at most
+// (n / d) 2^-53 < 1 / d.
+__device__ __forceinline__ int floor_div(double n, double d)
+{
+    return __builtin_amdgcn_readfirstlane((int)__builtin_floor(n / d));
+}
 // First list entry of slice s (slices split [0, total) as evenly as integers
-// allow).
+// allow).  s <= nw <= 2^20 and total < 2^31 (the host checks both), so the
+// products below are exact doubles under 2^51.
 __device__ __forceinline__ int slice_start(int s, int total, int nw)
 {
-    return (int)(((long long)s * total) / nw);
+    return floor_div((double)s * total, nw);
 }
 // Slice that holds list entry u: the largest s with slice_start(s) <= u.
 __device__ __forceinline__ int slice_of(int u, int total, int nw)
 {
-    return (int)((((long long)u + 1) * nw - 1) / total);
+    return floor_div((double)(u + 1) * nw - 1.0, total);
 }
 
 template <typename T, typename O, int D, int G>
@@ -542,20 +554,58 @@ struct WaveDecoder {
         }
     }
 
-    // Reduce the piece's per-lane state to per-head totals: afterwards every
-    // lane holds the exponential sum of head my_head in l_run, and lanes with
-    // r == 0 hold the summed output rows for their chunk c of every head.
+    // Values of the flattened [G][E] output rows a lane keeps after
+    // reduce_piece: G * D / 64 (one to sixteen).
+    static constexpr int kOut = G * D / 64;
+    static_assert(kOut >= 1 && (G * E) % kOut == 0, "scatter width");
+    __device__ float &acc_at(int i) { return o_acc[i / E][i % E]; }
+
+    // One reduce-scatter step over lane bit K on the first 2n flattened
+    // values: lanes with the bit clear keep the sums of values [0, n), lanes
+    // with it set those of [n, 2n), in slots [0, n).  The swap instructions
+    // exchange two registers between the lane halves in one instruction, so
+    // a step costs one swap and one add per value kept.
+    template <int K, int n>
+    __device__ void scatter_step()
+    {
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            const float x = acc_at(i), y = acc_at(i + n);
+            if constexpr (K == 5 || K == 4) {
+                const auto p =
+                    K == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                              false, false)
+                           : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y),
+                                                              false, false);
+                acc_at(i) = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+            } else {
+                static_assert(K == 3, "row bits start at lane bit 3");
+                const bool hi = (lane >> 3) & 1;
+                acc_at(i) = (hi ? y : x) + xor_partner<8>(hi ? x : y);
+            }
+        }
+    }
+
+    // Reduce the piece's per-lane state to per-head totals.  Every lane ends
+    // with the exponential sum of head my_head in l_run.  The output rows
+    // are reduce-scattered over the row bits of the lane index (LOG2L..5,
+    // highest first): lane (c, r) ends with kOut sums in o_acc's first
+    // flattened slots, those of flattened indices [r kOut, (r + 1) kOut) of
+    // column chunk c.  An all-reduce would cost two instructions per value at
+    // every step (plus a copy per swap); this costs two per value kept.
     __device__ void reduce_piece()
     {
         // Lanes that differ only in directly-summed row bits hold copies of
         // the same scores; count each score once.
         const float l_once = ((c >> CP) == 0) ? l_run : 0.0f;
         l_run = allreduce_bits<S::LOG2G, 6, OpSum>(l_once);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                o_acc[h][e] = allreduce_bits<S::LOG2L, 6, OpSum>(o_acc[h][e]);
+        constexpr int steps = 6 - S::LOG2L;
+        if constexpr (steps >= 1)
+            scatter_step<5, G * E / 2>();
+        if constexpr (steps >= 2)
+            scatter_step<4, G * E / 4>();
+        if constexpr (steps >= 3)
+            scatter_step<3, G * E / 8>();
     }
 
     __device__ O *out_rows(int b_, int g_) const
@@ -563,39 +613,55 @@ struct WaveDecoder {
         return (O *)a.out + ((size_t)b_ * a.num_kv_heads * G + (size_t)g_ * G) * D;
     }
 
-    __device__ void write_output() const
+    // Flattened index i of chunk c, as an offset into [G][D] rows.
+    __device__ int row_offset(int i) const { return (i / E) * D + c * E + i % E; }
+
+    __device__ void write_output()
     {
         O *dst = out_rows(b, g);
+        float inv_l[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float inv = 1.0f / read_lane(l_run, h);
-            if (r == 0) {
-                float v[E];
+        for (int h = 0; h < G; ++h)
+            inv_l[h] = 1.0f / read_lane(l_run, h);
+        // Groups of consecutive values inside one head.
+        constexpr int kGrp = kOut < E ? kOut : E;
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    v[e] = o_acc[h][e] * inv;
-                store_out<O, E>(dst + (size_t)h * D + c * E, v);
-            }
+        for (int j0 = 0; j0 < kOut; j0 += kGrp) {
+            const int i0 = r * kOut + j0;
+            const int h = i0 / E;
+            float inv = inv_l[0];
+#pragma unroll
+            for (int hh = 1; hh < G; ++hh)
+                inv = h == hh ? inv_l[hh] : inv;
+            float v[kGrp];
+#pragma unroll
+            for (int j = 0; j < kGrp; ++j)
+                v[j] = acc_at(j0 + j) * inv;
+            store_out_n<O, kGrp>(dst + row_offset(i0), v);
         }
     }
 
     // Record layout (fp32): o[G][D] unnormalised rows, then m[G], then l[G];
-    // REC floats per record (a multiple of four).
-    __device__ void store_record(float *rec) const
+    // REC floats per record (a multiple of four).  Every lane stores its kOut
+    // values, in 16-byte pieces where it holds four or more.
+    __device__ void store_record(float *rec)
     {
         const __amdgpu_buffer_rsrc_t rs = record_rsrc(rec, S::REC);
-        if (r == 0) {
+        constexpr int kGrp = kOut < 4 ? kOut : 4;
 #pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int k = 0; k < E / 4; ++k) {
-                    const u32x4 v{__float_as_uint(o_acc[h][4 * k]),
-                                  __float_as_uint(o_acc[h][4 * k + 1]),
-                                  __float_as_uint(o_acc[h][4 * k + 2]),
-                                  __float_as_uint(o_acc[h][4 * k + 3])};
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (h * D + c * E + 4 * k) * 4, 0,
-                                                           kDeviceScope);
-                }
+        for (int j0 = 0; j0 < kOut; j0 += kGrp) {
+            const int off = row_offset(r * kOut + j0) * 4;
+            if constexpr (kGrp == 4) {
+                const u32x4 v{__float_as_uint(acc_at(j0)), __float_as_uint(acc_at(j0 + 1)),
+                              __float_as_uint(acc_at(j0 + 2)), __float_as_uint(acc_at(j0 + 3))};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kDeviceScope);
+            } else if constexpr (kGrp == 2) {
+                const u32x2 v{__float_as_uint(acc_at(j0)), __float_as_uint(acc_at(j0 + 1))};
+                __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, kDeviceScope);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc_at(j0)), rs, off, 0,
+                                                      kDeviceScope);
+            }
         }
         if (lane < G) {
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), rs, (G * D + lane) * 4,

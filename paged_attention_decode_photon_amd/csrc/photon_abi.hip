@@ -169,6 +169,11 @@ photon_status plan_decode(const photon_decode_desc *d, Plan *plan)
     // waves, so the slice a wave gets is at most part_tokens.
     const int64_t chunks = ((int64_t)d->max_context_len + p.quantum - 1) / p.quantum;
     const int64_t upper = (int64_t)d->num_seqs * d->kv.num_kv_heads * chunks;
+    if (upper + (int64_t)photon::kDecodeBoundaryUnits * d->num_seqs * d->kv.num_kv_heads > INT32_MAX)
+        return fail(PHOTON_ERR_UNSUPPORTED,
+                    "%lld units of work (num_seqs * num_kv_heads * chunks of max_context_len) "
+                    "exceed the kernel's 32-bit indexing",
+                    (long long)upper);
     int64_t waves;
     if (d->partition_tokens > 0) {
         if (d->partition_tokens % p.quantum != 0)

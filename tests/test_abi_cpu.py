@@ -157,6 +157,8 @@ def test_workspace_size_formula():
     (dd(part=-32), pa.ERR_INVALID_ARG),
     (dd(b=-1), pa.ERR_INVALID_ARG),
     (dd(b=2049), pa.ERR_UNSUPPORTED),
+    # 2048 x 8 KV heads x 150,000 units of 32 tokens: past 32-bit unit indexing
+    (dd(b=2048, mb=300_000, maxctx=300_000 * 16), pa.ERR_UNSUPPORTED),
     (dd(bs=32), pa.ERR_UNSUPPORTED),
     (dd(flags=2), pa.ERR_INVALID_ARG),          # unknown flag bit
     (dd(flags=-1), pa.ERR_INVALID_ARG),
