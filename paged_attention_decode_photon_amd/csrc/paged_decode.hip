@@ -641,9 +641,9 @@ struct WaveDecoder {
         }
     }
 
-    // Record layout (fp32): o[G][D] unnormalised rows, then m[G], then l[G];
-    // REC floats per record (a multiple of four).  Every lane stores its kOut
-    // values, in 16-byte pieces where it holds four or more.
+    // Record layout (fp32): o[G][D] unnormalised rows, then (m, l) of each
+    // head; REC floats per record (a multiple of four).  Every lane stores
+    // its kOut values, in 16-byte pieces where it holds four or more.
     __device__ void store_record(float *rec)
     {
         const __amdgpu_buffer_rsrc_t rs = record_rsrc(rec, S::REC);
@@ -663,25 +663,68 @@ struct WaveDecoder {
                                                       kDeviceScope);
             }
         }
-        if (lane < G) {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), rs, (G * D + lane) * 4,
-                                                  0, kDeviceScope);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_run), rs,
-                                                  (G * D + G + lane) * 4, 0, kDeviceScope);
+        if (lane < G)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m_run), __float_as_uint(l_run)},
+                                                  rs, (G * D + 2 * lane) * 4, 0, kDeviceScope);
+    }
+
+    // Fold the records of slices [s_first, s_last] into one lane's running
+    // (m, lsum, o) for outputs i .. i+3 of head h, kBatch records per round
+    // trip.  Slots past s_last get an empty descriptor: their loads return
+    // zeros without touching memory, and with m = -inf they add exact zeros,
+    // so a call takes the same values whatever kBatch covers it in one pass.
+    template <int kBatch>
+    __device__ void fold_records(int s_first, int s_last, int first_role, int i, int h, float &m,
+                                 float &lsum, float (&o)[4]) const
+    {
+        for (int s0 = s_first; s0 <= s_last; s0 += kBatch) {
+            float mj[kBatch], lj[kBatch];
+            u32x4 oj[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int s = s0 + k;
+                const bool in = s <= s_last;
+                const int role = s == s_first ? first_role : 0;
+                const __amdgpu_buffer_rsrc_t rs =
+                    record_rsrc(a.ws_rec + ((size_t)s * 2 + role) * S::REC, in ? S::REC : 0);
+                oj[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 4, 0, kDeviceScope);
+                const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs, (G * D + 2 * h) * 4, 0,
+                                                                      kDeviceScope);
+                mj[k] = in ? __uint_as_float(ml[0]) : -INFINITY;
+                lj[k] = __uint_as_float(ml[1]);
+            }
+            float m_new = m;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                m_new = fmaxf(m_new, mj[k]);
+            const float rescale = __builtin_amdgcn_exp2f(m - m_new);
+            lsum *= rescale;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] *= rescale;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const float f = __builtin_amdgcn_exp2f(mj[k] - m_new);
+                lsum = __builtin_fmaf(f, lj[k], lsum);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = __builtin_fmaf(f, __uint_as_float(oj[k][e]), o[e]);
+            }
+            m = m_new;
         }
     }
 
     // Merge the records of every piece of segment (sb, sg), units [su0, su1),
     // in slice order, and write the normalised output.  Each lane folds four
-    // consecutive outputs of one head; kBatch records are loaded at a time
-    // (sixteen: one round trip for the 16 one-unit pieces of a batch-1
-    // segment of 512 tokens; the registers of the chunk loop are free here).
-    // The segment's units are [su0, su1) of the slice list, after its empty
-    // units, which start at sv0: a slice that starts at or after sv0 has this
-    // segment as its first piece.
+    // consecutive outputs of one head.  Up to eight records (every segment
+    // of the batch-16 workloads) are loaded in one pass of eight, more in
+    // passes of sixteen (one round trip for the 16 one-unit pieces of a
+    // batch-1 segment of 512 tokens; the registers of the chunk loop are free
+    // here).  The segment's units are [su0, su1) of the slice list, after its
+    // empty units, which start at sv0: a slice that starts at or after sv0
+    // has this segment as its first piece.
     __device__ void merge_segment(int sb, int sg, int sv0, int su0, int su1, int total, int nw) const
     {
-        constexpr int kBatch = 16;
         const int s_first = slice_of(su0, total, nw);
         const int s_last = slice_of(su1 - 1, total, nw);
         const int first_role = slice_start(s_first, total, nw) >= sv0 ? 0 : 1;
@@ -691,47 +734,16 @@ struct WaveDecoder {
             const int i = 4 * v;  // first of this lane's four outputs
             const int h = i / D;
             float m = -INFINITY, lsum = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            for (int s0 = s_first; s0 <= s_last; s0 += kBatch) {
-                float mj[kBatch], lj[kBatch];
-                u32x4 oj[kBatch];
-#pragma unroll
-                for (int k = 0; k < kBatch; ++k) {
-                    const int s = s0 + k;
-                    const bool in = s <= s_last;
-                    const int role = s == s_first ? first_role : 0;
-                    const __amdgpu_buffer_rsrc_t rs =
-                        record_rsrc(a.ws_rec + ((size_t)s * 2 + role) * S::REC, in ? S::REC : 0);
-                    oj[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 4, 0, kDeviceScope);
-                    mj[k] = __uint_as_float(
-                        __builtin_amdgcn_raw_buffer_load_b32(rs, (G * D + h) * 4, 0, kDeviceScope));
-                    lj[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        rs, (G * D + G + h) * 4, 0, kDeviceScope));
-                    if (!in)
-                        mj[k] = -INFINITY;
-                }
-                float m_new = m;
-#pragma unroll
-                for (int k = 0; k < kBatch; ++k)
-                    m_new = fmaxf(m_new, mj[k]);
-                const float rescale = __builtin_amdgcn_exp2f(m - m_new);
-                lsum *= rescale;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] *= rescale;
-#pragma unroll
-                for (int k = 0; k < kBatch; ++k) {
-                    const float f = __builtin_amdgcn_exp2f(mj[k] - m_new);
-                    lsum = __builtin_fmaf(f, lj[k], lsum);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o[e] = __builtin_fmaf(f, __uint_as_float(oj[k][e]), o[e]);
-                }
-                m = m_new;
-            }
+            if (s_last - s_first < 8)
+                fold_records<8>(s_first, s_last, first_role, i, h, m, lsum, o);
+            else
+                fold_records<16>(s_first, s_last, first_role, i, h, m, lsum, o);
             const float inv = 1.0f / lsum;
+            float r4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                dst[i + e] = Elem<O>::from_float(o[e] * inv);
+                r4[e] = o[e] * inv;
+            store_out_n<O, 4>(dst + i, r4);
         }
     }
 };
