@@ -392,6 +392,19 @@ struct TileState {
             o_acc[t] = mfma32<T>(va[t], bl, o_acc[t]);
     }
 
+    // O^T += V^T P^T for fp32 storage with the A operand loaded straight
+    // from memory: v[4 t + i] is V[token 4 gq + i][column 16 t + lr].
+    __device__ void pv_direct(const uint32_t (&v)[NW], const float (&p)[4])
+    {
+        static_assert(EB == 4 && NW == 4 * MT, "one dword per tile and token");
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v[4 * t + i]), p[i],
+                                                                o_acc[t], 0, 0, 0);
+    }
+
     // O^T += V^T P^T with V^T (D x 16 tokens, row stride VS) in LDS (fp32
     // storage; 16-bit V goes through pv_rows / pv_rows2).
     __device__ void pv(const T *vt, int lr, int gq, const float (&p)[4])
@@ -437,12 +450,11 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     constexpr int NL = QD * EB / 16;       // 16-byte loads per lane per K (or V) row part
     constexpr int NW = QD * EB / 4;        // dwords per lane per row part
     constexpr int MT = D / 16;             // 16-wide output column tiles
-    constexpr int VS = kTile + 4;          // LDS row stride of a transposed V tile (elements)
-    // One wave's V tile: transposed (D x 16, row stride VS) for fp32;
-    // row-major (16 x D, row stride VRS) for 16-bit, read back through the
-    // transposing LDS read.
+    // One wave's V tile for 16-bit storage: row-major (16 x D, row stride
+    // VRS), read back through the transposing LDS read.  fp32 V is loaded
+    // straight into the MFMA operand layout and needs none.
     constexpr int VRS = D + 16 / EB;
-    constexpr int VT_BYTES = EB == 4 ? D * VS * EB : kTile * VRS * EB;
+    constexpr int VT_BYTES = EB == 4 ? 0 : kTile * VRS * EB;
     constexpr int OB_BYTES = kTile * D * 4;
     constexpr int SMEM = (kMqWaves * VT_BYTES > kMqWaves * OB_BYTES) ? kMqWaves * VT_BYTES
                                                                      : kMqWaves * OB_BYTES;
@@ -517,11 +529,27 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const u32x4 kv = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16 * i, 0, 0);
-            const u32x4 vv = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16 * i, 0, 0);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < 4; ++k)
                 kw[4 * i + k] = kv[k];
-                vw[4 * i + k] = vv[k];
+        }
+        if constexpr (EB == 4) {
+            // V straight into the A operand of O^T += V^T P^T: dword 4 t + i
+            // is V[token 4 gq + i][column 16 t + lr] (four 64-byte runs per
+            // load; the block's 4 KiB are read once over the 16 loads).
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vw[4 * t + i] = __builtin_amdgcn_raw_buffer_load_b32(
+                        vrs, ((4 * gq + i) * D + 16 * t + lr) * EB, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const u32x4 vv = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16 * i, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    vw[4 * i + k] = vv[k];
             }
         }
     };
@@ -529,12 +557,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     // Scores, softmax update and P.V of block n from its loaded K and V.
     auto compute_block = [&](int n, const uint32_t (&kw)[NW], const uint32_t (&vw)[NW]) {
         const f32x4 sc = TS::scores(kw, qw);
-        if constexpr (EB == 4) {
-            // V^T into LDS: element (d, token lr) of this lane's quarter.
-#pragma unroll
-            for (int w = 0; w < NW; ++w)
-                vt[(gq * QD + w) * VS + lr] = __builtin_bit_cast(T, vw[w]);
-        } else {
+        if constexpr (EB == 2) {
             // V row lr, this lane's quarter, as it is (16-byte stores).
 #pragma unroll
             for (int i = 0; i < NL; ++i)
@@ -546,12 +569,13 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         const bool live[1] = {true};
         st.template update<1>(sv, live, (n + 1) * kTile - 1 <= tile_first_pos, n, row_ok, my_pos,
                               a.qscale, gq, p);
-        wave_sync();  // the V tile is complete
-        if constexpr (EB == 4)
-            st.pv(vt, lr, gq, p[0]);
-        else
+        if constexpr (EB == 4) {
+            st.pv_direct(vw, p[0]);  // V was loaded in the operand layout
+        } else {
+            wave_sync();  // the V tile is complete
             st.pv_rows(vt, VRS, lr, gq, p[0]);
-        wave_sync();  // reads of the V tile are done before the next block overwrites it
+            wave_sync();  // reads of the V tile are done before the next block overwrites it
+        }
     };
 
     // This wave's blocks n_begin + wave + 4 j, two in flight at all times:
