@@ -216,6 +216,22 @@ __device__ __forceinline__ int slice_of(int u, int total, int nw)
     return floor_div((double)(u + 1) * nw - 1.0, total);
 }
 
+// The slices holding a segment's records, in merge order.  The segment's
+// units are entries [su0, su1) of the slice list, after its empty units,
+// which start at sv0: a slice that starts at or after sv0 has the segment as
+// its first piece (record role 0), else as its second (role 1).
+struct SegmentSlices {
+    int first, last, first_role;
+};
+__device__ __forceinline__ SegmentSlices segment_slices(int sv0, int su0, int su1, int total, int nw)
+{
+    SegmentSlices ss;
+    ss.first = slice_of(su0, total, nw);
+    ss.last = slice_of(su1 - 1, total, nw);
+    ss.first_role = slice_start(ss.first, total, nw) >= sv0 ? 0 : 1;
+    return ss;
+}
+
 template <typename T, typename O, int D, int G>
 struct WaveDecoder {
     using S = Shape<T, D, G>;
@@ -720,14 +736,10 @@ struct WaveDecoder {
     // of the batch-16 workloads) are loaded in one pass of eight, more in
     // passes of sixteen (one round trip for the 16 one-unit pieces of a
     // batch-1 segment of 512 tokens; the registers of the chunk loop are free
-    // here).  The segment's units are [su0, su1) of the slice list, after its
-    // empty units, which start at sv0: a slice that starts at or after sv0
-    // has this segment as its first piece.
-    __device__ void merge_segment(int sb, int sg, int sv0, int su0, int su1, int total, int nw) const
+    // here).
+    __device__ void merge_segment(int sb, int sg, const SegmentSlices &ss) const
     {
-        const int s_first = slice_of(su0, total, nw);
-        const int s_last = slice_of(su1 - 1, total, nw);
-        const int first_role = slice_start(s_first, total, nw) >= sv0 ? 0 : 1;
+        const int s_first = ss.first, s_last = ss.last, first_role = ss.first_role;
         O *dst = out_rows(sb, sg);
         compiler_memory_barrier();
         for (int v = lane; v < G * D / 4; v += 64) {
@@ -914,7 +926,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     // the wave, and the count's result is only read at the end (merging
     // then, should this wave have completed the segment).
     bool pend = false, pend_count_now = false;
-    int pend_b = 0, pend_g = 0, pend_seg = 0, pend_nch = 0, pend_units = 0, pend_old = 0;
+    int pend_b = 0, pend_g = 0, pend_nch = 0, pend_units = 0, pend_old = 0;
+    SegmentSlices pend_slices{0, 0, 0};
     uint64_t pend_seen = 0;  // lane 0: what the pending piece's claim found
     while (true) {
         const int seq_end = end_of(b) + C * hkv * ne_of(b);
@@ -975,10 +988,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
                 pend_seen = seen;
                 pend_b = b;
                 pend_g = g;
-                pend_seg = seg_v0;
+                pend_slices = segment_slices(seg_v0, seg_v0 + C, seg_v0 + stride, total_v, nw);
                 pend_nch = nch;
                 pend_units = ch1 - ch0;
             } else {
+                // The merge's slice bounds, in the shadow of the stores and the count.
+                const SegmentSlices ss = segment_slices(seg_v0, seg_v0 + C, seg_v0 + stride, total_v, nw);
                 wait_vector_memory();
                 int done = 0;
                 if (lane == 0)
@@ -986,7 +1001,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
                                                ch1 - ch0);
                 done = __builtin_amdgcn_readfirstlane(done) + (ch1 - ch0);
                 if (done == nch) {
-                    w.merge_segment(b, g, seg_v0, seg_v0 + C, seg_v0 + stride, total_v, nw);
+                    w.merge_segment(b, g, ss);
                     if (lane == 0)
                         release_counter(&a.ws_count[(size_t)b * hkv + g]);
                 }
@@ -1003,7 +1018,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         }
     }
     if (pend && __builtin_amdgcn_readfirstlane(pend_old) + pend_units == pend_nch) {
-        w.merge_segment(pend_b, pend_g, pend_seg, pend_seg + C, pend_seg + C + pend_nch, total_v, nw);
+        w.merge_segment(pend_b, pend_g, pend_slices);
         if (lane == 0)
             release_counter(&a.ws_count[(size_t)pend_b * hkv + pend_g]);
     }
