@@ -686,14 +686,20 @@ struct WaveDecoder {
 
     // Fold the records of slices [s_first, s_last] into one lane's running
     // (m, lsum, o) for outputs i .. i+3 of head h, kBatch records per round
-    // trip.  Slots past s_last get an empty descriptor: their loads return
-    // zeros without touching memory, and with m = -inf they add exact zeros,
-    // so a call takes the same values whatever kBatch covers it in one pass.
+    // trip.  Slots past s_last load zeros without touching memory, and with
+    // m = -inf they add exact zeros, so a call takes the same values whatever
+    // kBatch covers it in one pass.
     template <int kBatch>
     __device__ void fold_records(int s_first, int s_last, int first_role, int i, int h, float &m,
                                  float &lsum, float (&o)[4]) const
     {
         for (int s0 = s_first; s0 <= s_last; s0 += kBatch) {
+            // One descriptor over the batch's records (two per slice, role 0
+            // then role 1), offsets in the vector operand so that the range
+            // check covers them: slots past s_last fall outside and load zeros.
+            const int nrec = 2 * (min(s_last + 1, s0 + kBatch) - s0);
+            const __amdgpu_buffer_rsrc_t rs =
+                record_rsrc(a.ws_rec + (size_t)s0 * 2 * S::REC, nrec * S::REC);
             float mj[kBatch], lj[kBatch];
             u32x4 oj[kBatch];
 #pragma unroll
@@ -701,10 +707,9 @@ struct WaveDecoder {
                 const int s = s0 + k;
                 const bool in = s <= s_last;
                 const int role = s == s_first ? first_role : 0;
-                const __amdgpu_buffer_rsrc_t rs =
-                    record_rsrc(a.ws_rec + ((size_t)s * 2 + role) * S::REC, in ? S::REC : 0);
-                oj[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 4, 0, kDeviceScope);
-                const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs, (G * D + 2 * h) * 4, 0,
+                const int rec = (2 * k + role) * S::REC * 4;
+                oj[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, rec + i * 4, 0, kDeviceScope);
+                const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs, rec + (G * D + 2 * h) * 4, 0,
                                                                       kDeviceScope);
                 mj[k] = in ? __uint_as_float(ml[0]) : -INFINITY;
                 lj[k] = __uint_as_float(ml[1]);
