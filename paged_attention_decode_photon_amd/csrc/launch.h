@@ -63,6 +63,14 @@ constexpr int decode_record_floats(int head_dim, int group)
 #define PHOTON_MQ_WIDE_TILES 4
 #endif
 constexpr int kWideTiles = PHOTON_MQ_WIDE_TILES;
+// Wavefronts per workgroup of the per-tile multi-query kernel (each takes
+// every kMqTileWaves-th block of the workgroup's split).  Four-token
+// verification at batch 16 at its best split, fp32 / bf16: 1 wave 29.8 /
+// 23.7 us, 2 waves 26.5 / 19.1 us, 4 waves 25.0 / 16.7 us.
+#ifndef PHOTON_MQ_TILE_WAVES
+#define PHOTON_MQ_TILE_WAVES 4
+#endif
+constexpr int kMqTileWaves = PHOTON_MQ_TILE_WAVES;
 
 // Sequences per call: the decode kernel keeps per-sequence prefix sums in LDS.
 constexpr int kMaxDecodeSeqs = 2048;

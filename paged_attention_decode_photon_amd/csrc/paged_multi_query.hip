@@ -421,29 +421,31 @@ struct TileState {
 };
 
 // Workgroup-level running max and exponential sum of tile row r, from the
-// four waves' statistics (the same values every lane forms in the merge).
-__device__ __forceinline__ float m_all_row(const float (&sm)[kMqWaves][kTile], int r)
+// W waves' statistics (the same values every lane forms in the merge).
+template <int W>
+__device__ __forceinline__ float m_all_row(const float (&sm)[W][kTile], int r)
 {
     float m = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kMqWaves; ++w)
+    for (int w = 0; w < W; ++w)
         m = fmaxf(m, sm[w][r]);
     return m;
 }
-__device__ __forceinline__ float l_all_row(const float (&sm)[kMqWaves][kTile],
-                                           const float (&sl)[kMqWaves][kTile], int r)
+template <int W>
+__device__ __forceinline__ float l_all_row(const float (&sm)[W][kTile], const float (&sl)[W][kTile],
+                                           int r)
 {
     const float m = m_all_row(sm, r);
     const float mu = m == -INFINITY ? 0.0f : m;
     float l = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMqWaves; ++w)
+    for (int w = 0; w < W; ++w)
         l += sl[w][r] * __builtin_amdgcn_exp2f(sm[w][r] - mu);
     return l;
 }
 
 template <typename T, typename O, int D, int G>
-__global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs a)
+__global__ __launch_bounds__(kMqTileWaves * 64) void paged_mq_kernel(MultiQueryArgs a)
 {
     constexpr int EB = sizeof(T);
     constexpr int QD = D / 4;              // head-dimension elements per lane
@@ -456,10 +458,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
     constexpr int VRS = D + 16 / EB;
     constexpr int VT_BYTES = EB == 4 ? 0 : kTile * VRS * EB;
     constexpr int OB_BYTES = kTile * D * 4;
-    constexpr int SMEM = (kMqWaves * VT_BYTES > kMqWaves * OB_BYTES) ? kMqWaves * VT_BYTES
-                                                                     : kMqWaves * OB_BYTES;
+    constexpr int W = kMqTileWaves;
+    constexpr int SMEM = (W * VT_BYTES > W * OB_BYTES) ? W * VT_BYTES : W * OB_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
-    __shared__ float stat_m[kMqWaves][kTile], stat_l[kMqWaves][kTile];
+    __shared__ float stat_m[W][kTile], stat_l[W][kTile];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -578,11 +580,11 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         }
     };
 
-    // This wave's blocks n_begin + wave + 4 j, two in flight at all times:
+    // This wave's blocks n_begin + wave + W j, two in flight at all times:
     // each block's registers are refilled with the block after next as soon
     // as the block has been used.
     {
-        constexpr int S = kMqWaves;
+        constexpr int S = W;
         uint32_t ka[NW], va[NW], kb[NW], vb[NW];
         int n = n_begin + wave;
         if (n < n_end)
@@ -603,7 +605,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         }
     }
 
-    // Merge the four waves' partial states of each row.
+    // Merge the W waves' partial states of each row.
     float l_row = allreduce_pair<16, OpSum>(st.l_lane);
     l_row = allreduce_pair<32, OpSum>(l_row);
     const float m_run = st.m_run;
@@ -627,10 +629,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
             ob[lr * D + 16 * t + 4 * gq + i] = st.o_acc[t][i] * f;
     __syncthreads();
 
-    // Sum the four partial rows: thread -> (row, D/16 columns).
-    constexpr int PER = D / 16;
-    const int orow = threadIdx.x >> 4;
-    const int c0 = (threadIdx.x & 15) * PER;
+    // Sum the W partial rows: thread -> (row, D / (4 W) columns).
+    constexpr int TPR = 4 * W;  // threads per row
+    constexpr int PER = D / TPR;
+    static_assert(PER % 4 == 0, "whole 16-byte pieces per thread");
+    const int orow = threadIdx.x / TPR;
+    const int c0 = (threadIdx.x % TPR) * PER;
     const int rr = tile * kTile + orow;
     float v[PER];
     {
@@ -639,7 +643,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
         for (int e = 0; e < PER; ++e) {
             float acc = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kMqWaves; ++w)
+            for (int w = 0; w < W; ++w)
                 acc += o0[(w * kTile + orow) * D + c0 + e];
             v[e] = acc;
         }
@@ -666,7 +670,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void paged_mq_kernel(MultiQueryArgs 
                 u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
                       __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])},
                 rs, (orow * D + c0 + 4 * k) * 4, 0, kSc1);
-        if ((threadIdx.x & 15) == 0) {
+        if (threadIdx.x % TPR == 0) {
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_all_row(stat_m, orow)), rs,
                                                   (kTile * D + orow) * 4, 0, kSc1);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_all_row(stat_m, stat_l, orow)),
@@ -1042,11 +1046,12 @@ hipError_t launch_mq_group(const MultiQueryArgs &a, hipStream_t stream)
         return hipGetLastError();
     }
     const dim3 grid((unsigned)a.max_tiles, yz, (unsigned)a.num_splits);
+    const dim3 tile_block(kMqTileWaves * 64);
     switch (a.group) {
-    case 1: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 2>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 4>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 8>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 1>), grid, tile_block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 2>), grid, tile_block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 4>), grid, tile_block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((paged_mq_kernel<T, O, D, 8>), grid, tile_block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

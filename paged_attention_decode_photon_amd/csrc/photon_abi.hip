@@ -278,7 +278,9 @@ photon_status plan_multi_query(const photon_multi_query_desc *d, MqPlan *plan)
     } else {
         const int64_t want = tiles > 0 ? (kMqTargetGroups + tiles - 1) / tiles : 1;
         sb = want > 1 ? (max_nblk + want - 1) / want : max_nblk;
-        sb = (sb + 7) / 8 * 8;  // whole steps: four waves, two blocks each
+        // whole steps: every wave of a workgroup two blocks
+        const int64_t step = 2 * (p.max_tiles < photon::kWideTiles ? photon::kMqTileWaves : 4);
+        sb = (sb + step - 1) / step * step;
         const int64_t min_sb = elem_bytes_of(d->kv.dtype) == 4 && p.max_tiles < photon::kWideTiles
                                    ? kMqMinSplitBlocksF32
                                    : kMqMinSplitBlocks;
