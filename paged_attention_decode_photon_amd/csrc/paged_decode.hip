@@ -148,6 +148,9 @@ __device__ __forceinline__ void wait_vector_memory()
 {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
+// s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt left at their
+// maxima): unlike an asm wait, the compiler's own wait bookkeeping sees it.
+constexpr int kWaitVmcnt0 = 0x0f70;
 // Compiler-only barrier for memory accesses.
 __device__ __forceinline__ void compiler_memory_barrier()
 {
@@ -291,12 +294,16 @@ struct WaveDecoder {
     }
 
     // Make the window hold blocks [n_first, n_last] (n_last - n_first < 64).
-    // Called at the start of a step, before its K/V loads are issued: the
-    // wait for a refreshed window then never holds up loads in flight.
+    // A refreshed window is waited for right here.  The load is conditional,
+    // so without this wait the compiler counts the window register as
+    // possibly pending wherever it is read and waits for every load in
+    // flight before each block lookup, the chunk in flight included: the
+    // next chunk would only be issued once the current one had arrived.
     __device__ void cover_blocks(int n_first, int n_last)
     {
-        if (n_last - win0 >= 64)
+        if (n_last - win0 >= 64) {
             load_table_window(n_first);
+        }
     }
 
     __device__ int block_at(int n) const { return __builtin_amdgcn_readlane(tbl_win, n - win0); }
@@ -322,6 +329,8 @@ struct WaveDecoder {
                     qf[hs][e] *= a.qscale;
             }
         }
+        // The window (and the query rows, in the same round trip) before the
+        // piece's first loads; see cover_blocks.
         new_pos = -1;
         m_run = -INFINITY;
         l_run = 0.0f;
@@ -335,14 +344,16 @@ struct WaveDecoder {
     // Issue the K and V loads of chunk ch (U blocks) of the current segment.
     // A block past the context gets an empty descriptor: its loads return
     // zeros without touching memory.
-    __device__ void load_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU]) const
+    // live == false (wave-uniform): every descriptor is empty, so the loads
+    // return zeros without touching memory.
+    __device__ void load_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU], bool live = true) const
     {
         const size_t tile_stride = (size_t)kBlockTokens * RB;
         __amdgpu_buffer_rsrc_t rk[S::U], rv[S::U];
 #pragma unroll
         for (int u = 0; u < S::U; ++u) {
             const int n = ch * S::U + u;
-            int rows = ctx - n * kBlockTokens;
+            int rows = live ? ctx - n * kBlockTokens : 0;
             rows = rows > kBlockTokens ? kBlockTokens : rows;
             int blk = 0;
             if (rows > 0)
@@ -476,19 +487,23 @@ struct WaveDecoder {
         append_settled = true;  // this chunk's loads are done, and so are older stores
     }
 
-    __device__ void issue_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU])
+    // live == false: a chunk past the piece's end, issued with empty
+    // descriptors (see run_chunks).
+    __device__ void issue_chunk(int ch, u32x4 (&kd)[NU], u32x4 (&vd)[NU], bool live = true)
     {
-        cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
-        if (append_pending) {  // the piece's first chunk: store the new row now
-            store_new_token();
-            append_pending = false;
-            append_settled = false;
+        if (live) {
+            cover_blocks(ch * S::U, (ch + 1) * S::U - 1);
+            if (append_pending) {  // the piece's first chunk: store the new row now
+                store_new_token();
+                append_pending = false;
+                append_settled = false;
+            }
+            // The chunk that holds the new row must see it: the stores are
+            // done once any chunk issued after them has been used, else wait.
+            if (new_pos >= ch * CT && new_pos < (ch + 1) * CT && !append_settled)
+                wait_vector_memory();
         }
-        // The chunk that holds the new row must see it: the stores are done
-        // once any chunk issued after them has been used, else wait here.
-        if (new_pos >= ch * CT && new_pos < (ch + 1) * CT && !append_settled)
-            wait_vector_memory();
-        load_chunk(ch, kd, vd);
+        load_chunk(ch, kd, vd, live);
     }
 
     // Chunks [ch0, ch1) of the current segment, two in flight: the next
@@ -496,6 +511,11 @@ struct WaveDecoder {
     // alternating).  With eight query heads per KV head the second set would
     // take the kernel past 256 VGPRs, i.e. below the two waves per SIMD the
     // automatic plan launches for 16-bit storage; those go one at a time.
+    //
+    // The next chunk's loads are issued on every iteration, past the piece's
+    // last chunk with empty descriptors (no memory access): with an issue
+    // that only some paths make, the compiler's waits for the current chunk
+    // count as if the next one were not in flight and wait for it as well.
     //
     // ctr: when not null, the piece's arrival counter, claimed right after the
     // first chunk's loads (one place in the code, so the compiler keeps the
@@ -511,18 +531,19 @@ struct WaveDecoder {
             u32x4 ka[NU], va[NU], kb[NU], vb[NU];
             issue_chunk(ch0, ka, va);
             claim();
-            for (int ch = ch0;;) {
-                if (ch + 1 < ch1)
-                    issue_chunk(ch + 1, kb, vb);
-                consume_chunk(ch, ka, va);
-                if (++ch >= ch1)
-                    break;
-                if (ch + 1 < ch1)
-                    issue_chunk(ch + 1, ka, va);
-                consume_chunk(ch, kb, vb);
-                if (++ch >= ch1)
-                    break;
-            }
+            if (ch0 + 1 >= ch1)
+                consume_chunk(ch0, ka, va);
+            else
+                for (int ch = ch0;;) {
+                    issue_chunk(ch + 1, kb, vb, ch + 1 < ch1);
+                    consume_chunk(ch, ka, va);
+                    if (++ch >= ch1)
+                        break;
+                    issue_chunk(ch + 1, ka, va, ch + 1 < ch1);
+                    consume_chunk(ch, kb, vb);
+                    if (++ch >= ch1)
+                        break;
+                }
         } else {
             {
                 u32x4 kd[NU], vd[NU];
