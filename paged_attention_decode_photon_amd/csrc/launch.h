@@ -13,7 +13,7 @@ namespace photon {
 #define PHOTON_DECODE_WAVES 4    // wavefronts per decode workgroup
 #endif
 #ifndef PHOTON_KV_LOAD_AUX
-#define PHOTON_KV_LOAD_AUX 0     // cache-policy bits of the K/V buffer loads
+#define PHOTON_KV_LOAD_AUX -1    // cache-policy bits of the K/V buffer loads; -1: rule below
 #endif
 #ifndef PHOTON_DECODE_CHUNK_BLOCKS
 #define PHOTON_DECODE_CHUNK_BLOCKS 0  // KV blocks per unit of work; 0: shape rule below
@@ -41,6 +41,19 @@ constexpr int decode_chunk_blocks(int elem_bytes, int head_dim, int group)
 // (the next chunk loads while the current one is used), except with eight
 // query heads per KV head, where a second set would cost occupancy.
 constexpr int decode_chunks_in_flight(int group) { return group < 8 ? 2 : 1; }
+
+// Cache-policy bits of the decode kernel's K/V loads: non-temporal (the nt
+// bit) with four or more query heads per KV head, none with fewer.  Measured
+// per call (fused step, both orders): nt is 5-12% faster with four or eight
+// query heads per KV head at head_dim 64 and 128, f32 and 16-bit, from
+// batch 16 up to 8 x 32K tokens; with two it is 5-30% slower (f32 head_dim
+// 64 and 128, 16-bit head_dim 128) except for 16-bit head_dim 64 (4%
+// faster).
+constexpr int kLoadNonTemporal = 2;
+constexpr int decode_kv_load_aux(int group)
+{
+    return PHOTON_KV_LOAD_AUX >= 0 ? PHOTON_KV_LOAD_AUX : group >= 4 ? kLoadNonTemporal : 0;
+}
 
 // Tokens one decode wavefront handles per loop step (the partition quantum).
 constexpr int decode_chunk_tokens(int elem_bytes, int head_dim, int group)
