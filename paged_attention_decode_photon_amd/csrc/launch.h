@@ -12,8 +12,11 @@ namespace photon {
 #ifndef PHOTON_DECODE_WAVES
 #define PHOTON_DECODE_WAVES 4    // wavefronts per decode workgroup
 #endif
-#ifndef PHOTON_KV_LOAD_AUX
-#define PHOTON_KV_LOAD_AUX -1    // cache-policy bits of the K/V buffer loads; -1: rule below
+#ifndef PHOTON_K_LOAD_AUX
+#define PHOTON_K_LOAD_AUX 0      // cache-policy bits of the decode K loads
+#endif
+#ifndef PHOTON_V_LOAD_AUX
+#define PHOTON_V_LOAD_AUX 2      // ... and of the V loads (2: the nt bit, see below)
 #endif
 #ifndef PHOTON_DECODE_CHUNK_BLOCKS
 #define PHOTON_DECODE_CHUNK_BLOCKS 0  // KV blocks per unit of work; 0: shape rule below
@@ -42,18 +45,14 @@ constexpr int decode_chunk_blocks(int elem_bytes, int head_dim, int group)
 // query heads per KV head, where a second set would cost occupancy.
 constexpr int decode_chunks_in_flight(int group) { return group < 8 ? 2 : 1; }
 
-// Cache-policy bits of the decode kernel's K/V loads: non-temporal (the nt
-// bit) with four or more query heads per KV head, none with fewer.  Measured
-// per call (fused step, both orders): nt is 5-12% faster with four or eight
-// query heads per KV head at head_dim 64 and 128, f32 and 16-bit, from
-// batch 16 up to 8 x 32K tokens; with two it is 5-30% slower (f32 head_dim
-// 64 and 128, 16-bit head_dim 128) except for 16-bit head_dim 64 (4%
-// faster).
-constexpr int kLoadNonTemporal = 2;
-constexpr int decode_kv_load_aux(int group)
-{
-    return PHOTON_KV_LOAD_AUX >= 0 ? PHOTON_KV_LOAD_AUX : group >= 4 ? kLoadNonTemporal : 0;
-}
+// Cache-policy bits of the decode kernel's K and V loads: V non-temporal
+// (the nt bit), K default.  Measured per call (fused step, both orders): nt
+// on V alone is 1-8% faster on every shape tried (f32 and 16-bit, head_dim
+// 64 and 128, two to eight query heads per KV head, batch 1 to 8 x 32K
+// tokens); nt on K as well gains a little more with four query heads per
+// KV head at f32 and loses 10-30% with two.
+constexpr int kDecodeKLoadAux = PHOTON_K_LOAD_AUX;
+constexpr int kDecodeVLoadAux = PHOTON_V_LOAD_AUX;
 
 // Tokens one decode wavefront handles per loop step (the partition quantum).
 constexpr int decode_chunk_tokens(int elem_bytes, int head_dim, int group)

@@ -369,11 +369,11 @@ struct WaveDecoder {
 #pragma unroll
         for (int i = 0; i < NU; ++i)
             kd[i] = __builtin_amdgcn_raw_buffer_load_b128(rk[i / NIB], k_off[i % NIB], 0,
-                                                          decode_kv_load_aux(G));
+                                                          kDecodeKLoadAux);
 #pragma unroll
         for (int i = 0; i < NU; ++i)
             vd[i] = __builtin_amdgcn_raw_buffer_load_b128(rv[i / NIB], v_off[i % NIB], 0,
-                                                          decode_kv_load_aux(G));
+                                                          kDecodeVLoadAux);
         // Keep every K and V load of the chunk ahead of the math (the
         // scheduler otherwise sinks part of V behind the scores, which costs
         // a second round trip per chunk).
