@@ -6,7 +6,7 @@
 // bound what a decode kernel reading the same bytes can reach.
 //
 // All use the decode kernel's memory instructions (16-byte raw buffer
-// loads, range-checked descriptors).  The gathers walk the sequence-major
+// loads, range-checked descriptors, V rows loaded non-temporal).  The gathers walk the sequence-major
 // list of (sequence, KV head, block) tiles and resolve up to 64 tiles at a
 // time with one table load per lane.  Three ways of handing out the list:
 //   - gather_kernel: an even split over wavefronts, like the decode kernel's
@@ -29,6 +29,7 @@ namespace photon {
 namespace {
 
 constexpr int kRawBufferWord3 = 0x00020000;  // raw, unswizzled buffer (gfx9 family)
+constexpr int kVLoadAux = 2;                 // nt bit on V loads, K plain (the decode kernel's policy)
 constexpr int kProbeWaves = 4;               // wavefronts per workgroup
 constexpr int kSetLoads = 8;                 // 16-byte loads per lane per register set (8 KiB/wave)
 constexpr int kMaxProbeSeqs = 64;
@@ -190,8 +191,8 @@ struct RegisterGather {
                     for (int i = 0; i < TL; ++i) {
                         d[(2 * t) * TL + i] =
                             __builtin_amdgcn_raw_buffer_load_b128(rk, (i * 64 + lane) * 16, 0, 0);
-                        d[(2 * t + 1) * TL + i] =
-                            __builtin_amdgcn_raw_buffer_load_b128(rv, (i * 64 + lane) * 16, 0, 0);
+                        d[(2 * t + 1) * TL + i] = __builtin_amdgcn_raw_buffer_load_b128(
+                            rv, (i * 64 + lane) * 16, 0, kVLoadAux);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kStagedWaves * 64) void gather_staged_kernel(Gather
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(slot + i * 1024), 16,
                                                          (i * 64 + lane) * 16, 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(slot + (TL + i) * 1024),
-                                                         16, (i * 64 + lane) * 16, 0, 0, 0);
+                                                         16, (i * 64 + lane) * 16, 0, 0, kVLoadAux);
             }
         };
 #pragma unroll
