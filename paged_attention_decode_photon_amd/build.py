@@ -39,12 +39,18 @@ COMMON = [
 ]
 
 
+# Per-source device flags.  The decode kernel's first two arguments (context
+# lengths, batch size) are preloaded into SGPRs at dispatch (gfx950 kernel
+# argument preloading; older firmware runs the compiler's fallback prologue).
+SOURCE_FLAGS = {"paged_decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     if src in HOST_SOURCES:
         cmd = [CXX, *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *COMMON, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"{cmd[0]} failed for {src}:\n{r.stderr}")

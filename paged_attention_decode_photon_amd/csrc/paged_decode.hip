@@ -183,11 +183,9 @@ struct KernelArgs {
     const void *k_new;    // fused decode step: [B][Hkv][D] rows to append; NULL otherwise
     const void *v_new;
     const int32_t *block_tables;
-    const int32_t *context_lens;
     void *out;
     uint64_t *ws_count;  // epoch-tagged arrival counters (arrival.h)
     float *ws_rec;
-    int num_seqs;
     int num_kv_heads;
     int max_blocks;
     int num_waves;
@@ -805,8 +803,14 @@ __device__ int2 block_inclusive_scan2(int2 v, int2 *wave_totals)
     return make_int2(v.x + before.x, v.y + before.y);
 }
 
+// The context lengths and the batch size come first, as arguments of their
+// own: the library builds this kernel with them preloaded into scalar
+// registers at dispatch, so the context-length load, the first link of the
+// kernel's chain of dependent loads, is issued without waiting for a load of
+// the kernel arguments (the other arguments are loaded meanwhile).
 template <typename T, typename O, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelArgs a)
+__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(
+    const int32_t *context_lens, int num_seqs, KernelArgs a)
 {
     using S = Shape<T, D, G>;
     constexpr int CT = S::CT;
@@ -820,7 +824,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     __shared__ __attribute__((aligned(16))) float p_lds[WAVES][CT][G];
     constexpr bool kEarlyClaimRows = S::EB == 2 && D == 64;
 
-    const int B = a.num_seqs;
+    const int B = num_seqs;
     const int hkv = a.num_kv_heads;
 
     // Per sequence: its context length, and the inclusive prefix sums of
@@ -833,7 +837,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
     const bool small = B <= 64;
     int r_ctx = 0, r_end = 0, r_ne = 0;
     if (small) {
-        const int cl = lane < B ? a.context_lens[lane] : 0;
+        const int cl = lane < B ? context_lens[lane] : 0;
         r_ctx = cl;
         r_end = wave_inclusive_sum(hkv * ((cl + CT - 1) / CT));
         r_ne = wave_inclusive_sum(cl > 0 ? 1 : 0);
@@ -846,7 +850,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(KernelA
         int cls[kMaxPer];
 #pragma unroll
         for (int j = 0; j < kMaxPer; ++j)
-            cls[j] = (j < per && first + j < B) ? a.context_lens[first + j] : 0;
+            cls[j] = (j < per && first + j < B) ? context_lens[first + j] : 0;
         int2 mine = make_int2(0, 0);
 #pragma unroll
         for (int j = 0; j < kMaxPer; ++j) {
@@ -1060,18 +1064,16 @@ hipError_t launch_typed(const DecodeArgs &d, hipStream_t stream)
     a.k_new = d.k_new;
     a.v_new = d.v_new;
     a.block_tables = d.block_tables;
-    a.context_lens = d.context_lens;
     a.out = d.out;
     a.ws_count = d.ws_count;
     a.ws_rec = d.ws_rec;
-    a.num_seqs = d.num_seqs;
     a.num_kv_heads = d.num_kv_heads;
     a.max_blocks = d.max_blocks;
     a.num_waves = d.num_waves;
     a.qscale = d.qscale;
     a.epoch = d.epoch;
     hipLaunchKernelGGL((paged_decode_kernel<T, O, D, G>), dim3(d.num_waves / kDecodeWaves),
-                       dim3(kDecodeWaves * 64), 0, stream, a);
+                       dim3(kDecodeWaves * 64), 0, stream, d.context_lens, d.num_seqs, a);
     return hipGetLastError();
 }
 
