@@ -148,9 +148,6 @@ __device__ __forceinline__ void wait_vector_memory()
 {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
-// s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt left at their
-// maxima): unlike an asm wait, the compiler's own wait bookkeeping sees it.
-constexpr int kWaitVmcnt0 = 0x0f70;
 // Compiler-only barrier for memory accesses.
 __device__ __forceinline__ void compiler_memory_barrier()
 {
