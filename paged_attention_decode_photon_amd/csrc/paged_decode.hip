@@ -90,11 +90,14 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // Fewest units a wavefront's slice holds while more than kMinWaves waves
 // would take part: measured best among 1-6 on the batch-16 (fp32 and bf16),
 // ragged batch-64 and long-context workloads.  Small calls keep kMinWaves
-// waves (one per CU), since there the latency of a wave's chain of chunks
-// dominates: batch 1 at 512 tokens takes 10.5 us with one unit per wave
-// against 14.3 us with five.
+// waves (or one per unit), since there the latency of a wave's chain of
+// chunks dominates: batch 1 at 512 tokens takes 10.5 us with one unit per
+// wave against 14.3 us with five.  128 rather than 256: fewer slices per
+// segment, so fewer records to merge (batch 1 at 2048 tokens 13.4 -> 11.9 us,
+// batch 2 f32 13.9 -> 12.2 us, bf16 11.2 -> 9.3 us; batch 1 at 512 tokens,
+// batch 4 and up unchanged).
 constexpr int kMinUnitsPerWave = 5;
-constexpr int kMinWaves = 256;
+constexpr int kMinWaves = 128;
 // Work a wavefront is charged for starting on a segment, in units: a piece
 // change costs a record, an arrival and a fresh first round trip, so in a
 // batch of at least kChargeFromUnits units each non-empty segment is counted

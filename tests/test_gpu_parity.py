@@ -571,14 +571,15 @@ def contexts_with_chunks(rng, b, target, ct=32, most=5):
 
 
 @pytest.mark.parametrize("b", [64, 65])
-@pytest.mark.parametrize("target", [95, 96, 97, 160])
+@pytest.mark.parametrize("target", [47, 48, 49, 80, 81, 160])
 @pytest.mark.parametrize("part", [0, 64])
 def test_split_regimes_around_the_boundary_charge(pa, b, target, part):
     # 32 query / 8 KV heads, D 64: 32-token units, 8 units per 32-token
-    # stretch of a sequence.  96 stretches (768 units) is where the split
-    # starts charging a segment change, 160 (1280 units) where slices reach
-    # five units; 64 sequences keep the prefix sums in registers, 65 use the
-    # workgroup's LDS.  Empty contexts are mixed in.
+    # stretch of a sequence.  48 stretches (384 units, three per slice at
+    # the 128-wave floor) is where the split starts charging a segment
+    # change, 80 (640 units) where slices reach five units; 64 sequences
+    # keep the prefix sums in registers, 65 use the workgroup's LDS.  Empty
+    # contexts are mixed in.
     rng = np.random.default_rng(1000 + 10 * b + target + part)
     ctx = contexts_with_chunks(rng, b, target)
     q, kc, vc, tables, ctx = random_case(rng, np.float32, 0, 32, 8, 64, ctx_list=ctx)
@@ -592,7 +593,7 @@ def test_split_regimes_around_the_boundary_charge(pa, b, target, part):
 def test_split_regimes_bf16_fused_step(pa, b):
     # the same boundary for bf16 storage through the fused append + decode
     rng = np.random.default_rng(2000 + b)
-    ctx = contexts_with_chunks(rng, b, 97)
+    ctx = contexts_with_chunks(rng, b, 49)
     ctx = np.maximum(ctx, 1).astype(np.int32)
     q, kc, vc, tables, ctx = random_case(rng, di.BF16, 0, 32, 8, 64, ctx_list=ctx)
     k_new = di.cast(rng.standard_normal((b, 8, 64)), di.BF16)
