@@ -607,3 +607,30 @@ def test_split_regimes_bf16_fused_step(pa, b):
     torch.cuda.synchronize()
     assert_close(host(out), ref, di.BF16, f"fused B={b}")
     assert host(kcd).tobytes() == kw.tobytes() and host(vcd).tobytes() == vw.tobytes()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("part", [32, 64, 96, 128, 160])
+def test_pieces_of_one_to_five_chunks(pa, dtype, part):
+    # Slices of part/32 chunks over contexts of 1-192 tokens give pieces of
+    # one to five 32-token chunks, ragged at both ends: the decode loop's
+    # one-chunk path, and its exits after an even and after an odd number of
+    # chunks (the next chunk's loads are issued before the current one is
+    # used, alternating two register sets).  Plain call and fused step.
+    rng = np.random.default_rng(3000 + part)
+    ctx = rng.integers(1, 6 * 32 + 1, 24).astype(np.int32)
+    q, kc, vc, tables, ctx = random_case(rng, dtype, 0, 32, 8, 64, ctx_list=ctx)
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    assert_close(gpu_decode(pa, q, kc, vc, tables, ctx, 0.125, part=part), ref, dtype,
+                 f"part={part}")
+    k_new = di.cast(rng.standard_normal((len(ctx), 8, 64)), dtype)
+    v_new = di.cast(rng.standard_normal((len(ctx), 8, 64)), dtype)
+    kw, vw = oracle.kv_cache_write(k_new, v_new, derived_slots(tables, ctx), kc, vc)
+    ref = oracle.paged_attn_decode(q, kw, vw, tables, ctx, 0.125)
+    kcd, vcd = dev(kc), dev(vc)
+    out = pa.paged_attn_decode_step(dev(q), dev(k_new), dev(v_new), kcd, vcd, dev(tables),
+                                    dev(ctx), 0.125, max_context_len=int(ctx.max()),
+                                    partition_tokens=part)
+    torch.cuda.synchronize()
+    assert_close(host(out), ref, dtype, f"fused part={part}")
+    assert host(kcd).tobytes() == kw.tobytes() and host(vcd).tobytes() == vw.tobytes()
