@@ -510,10 +510,12 @@ struct WaveDecoder {
     // take the kernel past 256 VGPRs, i.e. below the two waves per SIMD the
     // automatic plan launches for 16-bit storage; those go one at a time.
     //
-    // The next chunk's loads are issued on every iteration, past the piece's
-    // last chunk with empty descriptors (no memory access): with an issue
-    // that only some paths make, the compiler's waits for the current chunk
-    // count as if the next one were not in flight and wait for it as well.
+    // Inside the loop the next chunk's loads are issued on every iteration,
+    // past the piece's last chunk with empty descriptors (no memory access):
+    // with an issue that only some paths make, the compiler's waits for the
+    // current chunk count as if the next one were not in flight and wait for
+    // it as well.  A one-chunk piece takes a path of its own, so that it
+    // issues no empty chunk.
     //
     // ctr: when not null, the piece's arrival counter, claimed right after the
     // first chunk's loads (one place in the code, so the compiler keeps the
