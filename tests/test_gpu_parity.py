@@ -634,3 +634,26 @@ def test_pieces_of_one_to_five_chunks(pa, dtype, part):
     torch.cuda.synchronize()
     assert_close(host(out), ref, dtype, f"fused part={part}")
     assert host(kcd).tobytes() == kw.tobytes() and host(vcd).tobytes() == vw.tobytes()
+
+
+@pytest.mark.parametrize("dtype", [np.float32, di.BF16])
+@pytest.mark.parametrize("n", [2048, 4103, 8192])
+def test_one_long_sequence(pa, dtype, n):
+    # Batch 1 with 32 query / 8 KV heads: 512-2048 units over 128 or more
+    # waves, so each of the eight segments is cut into 16 or more slices
+    # (several merge passes) and, from 384 units on, segment changes are
+    # charged.  Plain call and fused step.
+    rng = np.random.default_rng(4000 + n)
+    q, kc, vc, tables, ctx = random_case(rng, dtype, 0, 32, 8, 64, ctx_list=[n])
+    ref = oracle.paged_attn_decode(q, kc, vc, tables, ctx, 0.125)
+    assert_close(gpu_decode(pa, q, kc, vc, tables, ctx, 0.125), ref, dtype, f"n={n}")
+    k_new = di.cast(rng.standard_normal((1, 8, 64)), dtype)
+    v_new = di.cast(rng.standard_normal((1, 8, 64)), dtype)
+    kw, vw = oracle.kv_cache_write(k_new, v_new, derived_slots(tables, ctx), kc, vc)
+    ref = oracle.paged_attn_decode(q, kw, vw, tables, ctx, 0.125)
+    kcd, vcd = dev(kc), dev(vc)
+    out = pa.paged_attn_decode_step(dev(q), dev(k_new), dev(v_new), kcd, vcd, dev(tables),
+                                    dev(ctx), 0.125, max_context_len=n)
+    torch.cuda.synchronize()
+    assert_close(host(out), ref, dtype, f"fused n={n}")
+    assert host(kcd).tobytes() == kw.tobytes() and host(vcd).tobytes() == vw.tobytes()
